@@ -1,0 +1,379 @@
+// Host side of the C ABI declared in include/moe_fp4.h: argument validation
+// (pure host code, run before any HIP call), workspace carve-up and the launch
+// sequence of each entry point.  All launches go to the caller's stream; no
+// call synchronises or copies to the host.
+#include "moe_fp4.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_NULL_ARG;
+  if (c->tokens < 0) return MOE_ERR_BAD_SHAPE;
+  if (c->hidden < 128 || c->hidden > 16384 || c->hidden % 128) return MOE_ERR_BAD_SHAPE;
+  if (c->inter < 128 || c->inter > 16384 || c->inter % 128) return MOE_ERR_BAD_SHAPE;
+  if (c->n_experts < 1 || c->n_experts > 512) return MOE_ERR_BAD_SHAPE;
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MOE_ERR_BAD_SHAPE;
+  if (c->tokens * (int64_t)c->top_k >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  if (!std::isfinite(c->route_scale)) return MOE_ERR_BAD_SHAPE;
+  if (!(c->swiglu_limit > 0.f)) return MOE_ERR_BAD_SHAPE;  // NaN fails too; +inf allowed
+  if (c->route_mode != MOE_ROUTE_SQRTSOFTPLUS && c->route_mode != MOE_ROUTE_HASH)
+    return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+// Sequential carve-up of a workspace; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct RouteWs {
+  int32_t* perm_scratch;
+  float* logits;
+};
+RouteWs carve_route(Carver& cv, const moe_config& c) {
+  const int64_t P = c.tokens * c.top_k;
+  RouteWs r;
+  r.perm_scratch = cv.take<int32_t>(permute_scratch_bytes(P, c.n_experts) / sizeof(int32_t) + 1);
+  r.logits = cv.take<float>(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS ? (size_t)c.tokens * c.n_experts : 0);
+  return r;
+}
+
+struct FfnWs {
+  int32_t* mtile_off;
+  uint8_t* hq;
+  uint8_t* hs;
+};
+FfnWs carve_ffn(Carver& cv, const moe_config& c) {
+  const int64_t P = c.tokens * c.top_k;
+  FfnWs f;
+  f.mtile_off = cv.take<int32_t>(c.n_experts + 1);
+  f.hq = cv.take<uint8_t>((size_t)P * c.inter);
+  f.hs = cv.take<uint8_t>((size_t)P * (c.inter / 128));
+  return f;
+}
+
+struct LayerWs {
+  RouteWs route;
+  moe_routing routing;
+  uint8_t* xq;
+  uint8_t* xs;
+  FfnWs ffn;
+  float* o;
+  uint16_t* hsh;
+  float* ysh;
+};
+LayerWs carve_layer(Carver& cv, const moe_config& c) {
+  const int64_t P = c.tokens * c.top_k;
+  LayerWs l;
+  l.route = carve_route(cv, c);
+  l.routing.topk_idx = cv.take<int32_t>(P);
+  l.routing.topk_w = cv.take<float>(P);
+  l.routing.expert_offsets = cv.take<int32_t>(c.n_experts + 1);
+  l.routing.sorted_pairs = cv.take<int32_t>(P);
+  l.routing.pair_pos = cv.take<int32_t>(P);
+  l.xq = cv.take<uint8_t>((size_t)c.tokens * c.hidden);
+  l.xs = cv.take<uint8_t>((size_t)c.tokens * (c.hidden / 128));
+  l.ffn = carve_ffn(cv, c);
+  l.o = cv.take<float>((size_t)P * c.hidden);
+  l.hsh = cv.take<uint16_t>((size_t)c.tokens * c.inter);
+  l.ysh = cv.take<float>((size_t)c.tokens * c.hidden);
+  return l;
+}
+
+// Device architecture check, cached per device (0 unknown, 1 gfx950, 2 other).
+std::atomic<int> g_arch[64];
+
+moe_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_ARCH;
+  int v = g_arch[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? MOE_OK : MOE_ERR_ARCH;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                   \
+  do {                                                  \
+    hipError_t _e = (expr);                             \
+    if (_e != hipSuccess) return MOE_ERR_HIP;           \
+  } while (0)
+
+moe_status check_routing_ptrs(const moe_routing* r) {
+  if (!r->topk_idx || !r->topk_w || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
+    return MOE_ERR_NULL_ARG;
+  if (!aligned16(r->topk_idx) || !aligned16(r->topk_w) || !aligned16(r->expert_offsets) ||
+      !aligned16(r->sorted_pairs) || !aligned16(r->pair_pos))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_expert_weights* w) {
+  if (!w) return MOE_ERR_NULL_ARG;
+  const void* ps[6] = {w->w1, w->w1_scale, w->w3, w->w3_scale, w->w2, w->w2_scale};
+  for (const void* p : ps)
+    if (!p) return MOE_ERR_NULL_ARG;
+  for (const void* p : ps)
+    if (!aligned16(p)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+// Tokens per m-tile of the grouped GEMMs, from the mean pairs per expert.
+int choose_bm(const moe_config& c) {
+  const int64_t P = c.tokens * c.top_k;
+  return P <= (int64_t)32 * c.n_experts ? 16 : 64;
+}
+
+moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t* wg,
+                         const float* bias, const int64_t* ids, const float* logits_in,
+                         float* logits_out, const moe_routing& r, const RouteWs& ws,
+                         hipStream_t st) {
+  const int64_t T = c.tokens, P = T * c.top_k;
+  if (c.route_mode == MOE_ROUTE_HASH) {
+    MOE_TRY(launch_hash_route(ids, T, c.n_experts, c.top_k, c.route_scale, c.hash_seed,
+                              r.topk_idx, r.topk_w, st));
+  } else {
+    const float* z = logits_in;
+    if (!z) {
+      float* dst = logits_out ? logits_out : ws.logits;
+      MOE_TRY(launch_router_gemm(x, wg, dst, T, c.hidden, c.n_experts, st));
+      z = dst;
+    }
+    MOE_TRY(launch_score_topk(z, bias, T, c.n_experts, c.top_k, c.route_scale, r.topk_idx,
+                              r.topk_w, st));
+  }
+  MOE_TRY(launch_permute(r.topk_idx, P, c.n_experts, r.expert_offsets, r.sorted_pairs,
+                         r.pair_pos, ws.perm_scratch, st));
+  return MOE_OK;
+}
+
+moe_status enqueue_ffn(const moe_config& c, const uint8_t* xq, const uint8_t* xs,
+                       const moe_routing& r, const moe_expert_weights& w, void* out, int out_fp32,
+                       uint8_t* hq, uint8_t* hs, int32_t* mtile_off, hipStream_t st) {
+  const int64_t P = c.tokens * c.top_k;
+  if (P == 0) return MOE_OK;
+  const int bm = choose_bm(c);
+  const int64_t mt_max64 = (P + bm - 1) / bm + std::min<int64_t>(c.n_experts, P);
+  const int mt_max = (int)mt_max64;
+  MOE_TRY(launch_tile_prefix(r.expert_offsets, c.n_experts, bm, mtile_off, st));
+  ExpertGemmArgs a{};
+  a.expert_offsets = r.expert_offsets;
+  a.sorted_pairs = r.sorted_pairs;
+  a.mtile_off = mtile_off;
+  a.E = c.n_experts;
+  a.top_k = c.top_k;
+  a.P = P;
+  a.limit = c.swiglu_limit;
+  // GEMM1: x (FP8) x [w1 | w3] -> clamped SwiGLU -> hq, hs
+  a.a = xq;
+  a.a_scale = xs;
+  a.w = w.w1;
+  a.w_scale = w.w1_scale;
+  a.w3 = w.w3;
+  a.w3_scale = w.w3_scale;
+  a.K = c.hidden;
+  a.N = c.inter;
+  a.hq = hq;
+  a.hs = hs;
+  MOE_TRY(launch_expert_gemm1(a, bm, mt_max, st));
+  // GEMM2: hq (FP8) x w2 -> out
+  ExpertGemmArgs b = a;
+  b.a = hq;
+  b.a_scale = hs;
+  b.w = w.w2;
+  b.w_scale = w.w2_scale;
+  b.w3 = nullptr;
+  b.w3_scale = nullptr;
+  b.K = c.inter;
+  b.N = c.hidden;
+  b.out = out;
+  b.out_fp32 = out_fp32;
+  MOE_TRY(launch_expert_gemm2(b, bm, mt_max, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL_ARG: return "MOE_ERR_NULL_ARG: a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "MOE_ERR_BAD_SHAPE: a size is outside the supported range";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below moe_workspace_size()";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: combination not implemented";
+    case MOE_ERR_ARCH: return "MOE_ERR_ARCH: the current device is not gfx950 (MI355X)";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call or kernel launch failed";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_size(const moe_config* cfg, moe_op op) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  Carver cv(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE: carve_route(cv, *cfg); break;
+    case MOE_OP_EXPERT_FFN: carve_ffn(cv, *cfg); break;
+    case MOE_OP_LAYER: carve_layer(cv, *cfg); break;
+    default: return 0;
+  }
+  return cv.off;
+}
+
+moe_status moe_quant_act(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q,
+                         uint8_t* scale, void* stream) {
+  if (rows < 0 || cols < 128 || cols % 128 || cols > (1 << 20)) return MOE_ERR_BAD_SHAPE;
+  if (rows > 0 && (!x || !q || !scale)) return MOE_ERR_NULL_ARG;
+  if (rows > 0 && (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)))
+    return MOE_ERR_MISALIGNED;
+  if (rows == 0) return MOE_OK;
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+  return hip_status(launch_quant_act(x, rows, cols, q, scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                     const float* bias, const int64_t* token_ids, const float* logits_in,
+                     float* logits_out, const moe_routing* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (!out) return MOE_ERR_NULL_ARG;
+  if ((s = check_routing_ptrs(out)) != MOE_OK) return s;
+  if (c.route_mode == MOE_ROUTE_HASH) {
+    if (c.tokens > 0 && !token_ids) return MOE_ERR_NULL_ARG;
+  } else if (!logits_in && c.tokens > 0) {
+    if (!x || !w_gate) return MOE_ERR_NULL_ARG;
+    if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_MISALIGNED;
+  }
+  if (logits_out && !aligned16(logits_out)) return MOE_ERR_MISALIGNED;
+  if (logits_in && !aligned16(logits_in)) return MOE_ERR_MISALIGNED;
+  const size_t need = moe_workspace_size(cfg, MOE_OP_ROUTE);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need && !ws) return MOE_ERR_NULL_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  if ((s = check_device()) != MOE_OK) return s;
+  Carver cv(ws);
+  RouteWs rws = carve_route(cv, c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (logits_in && logits_out && c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && c.tokens > 0) {
+    MOE_TRY(hipMemcpyAsync(logits_out, logits_in, (size_t)c.tokens * c.n_experts * sizeof(float),
+                           hipMemcpyDeviceToDevice, st));
+  }
+  return enqueue_route(c, x, w_gate, bias, token_ids, logits_in, logits_out, *out, rws, st);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const uint8_t* xq, const uint8_t* xs,
+                          const moe_routing* r, const moe_expert_weights* w, void* out_pairs,
+                          uint8_t* hq_out, uint8_t* hs_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (!r || !w) return MOE_ERR_NULL_ARG;
+  if ((s = check_weights(w)) != MOE_OK) return s;
+  if (!r->expert_offsets || !r->sorted_pairs) return MOE_ERR_NULL_ARG;
+  if (!aligned16(r->expert_offsets) || !aligned16(r->sorted_pairs)) return MOE_ERR_MISALIGNED;
+  if ((hq_out == nullptr) != (hs_out == nullptr)) return MOE_ERR_NULL_ARG;
+  if (c.tokens > 0) {
+    if (!xq || !xs || !out_pairs) return MOE_ERR_NULL_ARG;
+    if (!aligned16(xq) || !aligned16(xs) || !aligned16(out_pairs)) return MOE_ERR_MISALIGNED;
+    if (hq_out && (!aligned16(hq_out) || !aligned16(hs_out))) return MOE_ERR_MISALIGNED;
+  }
+  const size_t need = moe_workspace_size(cfg, MOE_OP_EXPERT_FFN);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need && !ws) return MOE_ERR_NULL_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  if ((s = check_device()) != MOE_OK) return s;
+  Carver cv(ws);
+  FfnWs f = carve_ffn(cv, c);
+  uint8_t* hq = hq_out ? hq_out : f.hq;
+  uint8_t* hs = hs_out ? hs_out : f.hs;
+  return enqueue_ffn(c, xq, xs, *r, *w, out_pairs, c.out_fp32, hq, hs, f.mtile_off,
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                     const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
+                     const moe_shared_weights* shared, uint16_t* y,
+                     const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if ((s = check_weights(w)) != MOE_OK) return s;
+  if (c.tokens > 0) {
+    if (!x || !y) return MOE_ERR_NULL_ARG;
+    if (!aligned16(x) || !aligned16(y)) return MOE_ERR_MISALIGNED;
+    if (c.route_mode == MOE_ROUTE_HASH) {
+      if (!token_ids) return MOE_ERR_NULL_ARG;
+    } else {
+      if (!w_gate) return MOE_ERR_NULL_ARG;
+      if (!aligned16(w_gate) || (bias && !aligned16(bias))) return MOE_ERR_MISALIGNED;
+    }
+  }
+  if (shared) {
+    if (!shared->w1 || !shared->w3 || !shared->w2) return MOE_ERR_NULL_ARG;
+    if (!aligned16(shared->w1) || !aligned16(shared->w3) || !aligned16(shared->w2))
+      return MOE_ERR_MISALIGNED;
+  }
+  if (routing_out && (s = check_routing_ptrs(routing_out)) != MOE_OK) return s;
+  const size_t need = moe_workspace_size(cfg, MOE_OP_LAYER);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need && !ws) return MOE_ERR_NULL_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  if ((s = check_device()) != MOE_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  LayerWs l = carve_layer(cv, c);
+  const moe_routing& r = routing_out ? *routing_out : l.routing;
+  if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st)) != MOE_OK)
+    return s;
+  if (c.tokens == 0) return MOE_OK;
+  MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
+  if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st)) !=
+      MOE_OK)
+    return s;
+  const float* ysh = nullptr;
+  if (shared) {
+    MOE_TRY(launch_shared_up(x, shared->w1, shared->w3, l.hsh, c.tokens, c.hidden, c.inter,
+                             c.swiglu_limit, st));
+    MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, c.tokens, c.hidden, c.inter, st));
+    ysh = l.ysh;
+  }
+  MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, y, c.tokens, c.hidden, c.top_k, st));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// bf16 GEMMs of the layer: the router logits (the gate stays bf16: the
+// PTPC-FP8 article's 排除清单 excludes *ffn.gate* from quantization) and the
+// shared expert ("DeepSeek-V4-Flash-SI" card: 1 shared expert, non-expert
+// weights bf16, SwiGLU clamped to +-10).
+//
+// C[t][n] = sum_k X[t][k] * W[n][k] with v_mfma_f32_16x16x32_bf16: weight rows
+// are the A operand (lane l: row l%16, 8 consecutive K), token rows the B
+// operand (lane l: token l%16, the same 8 K); fp32 accumulation.  Each wave
+// owns TPW 16-row weight tiles and streams them over the whole K with 16-byte
+// loads straight into operand registers; token rows (MT 16-row sub-tiles) are
+// read the same way and are shared through L2.
+//   EPI_F32    out[t][n] fp32 (router logits, shared down projection)
+//   EPI_SWIGLU tiles 0..TPW/2-1 read w1 rows, the rest w3 rows of the same
+//              columns; out[t][n] = bf16(silu(clip(g)) * clip(u))
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
+
+__device__ __forceinline__ v4f mfma_bf16(const uint4& a, const uint4& b, v4f acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+template <int EPI, int TPW, int MT>
+__global__ __launch_bounds__(256) void bf16_gemm_kernel(const uint16_t* __restrict__ X,
+                                                        const uint16_t* __restrict__ W,
+                                                        const uint16_t* __restrict__ W3,
+                                                        void* __restrict__ out, int64_t M, int N,
+                                                        int K, float limit) {
+  constexpr int BM = 16 * MT;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  // rows (EPI_F32) or h columns (EPI_SWIGLU) covered by this wave
+  constexpr int WROWS = EPI == EPI_SWIGLU ? 8 * TPW : 16 * TPW;
+  const int n0 = blockIdx.x * 4 * WROWS + wv * WROWS;
+  if (n0 >= N) return;  // whole wave idle; no barriers in this kernel
+
+  const uint16_t* wp[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    int row;
+    const uint16_t* base;
+    if (EPI == EPI_SWIGLU) {
+      row = n0 + 16 * (t % (TPW / 2)) + col;
+      base = t < TPW / 2 ? W : W3;
+    } else {
+      row = n0 + 16 * t + col;
+      base = W;
+    }
+    if (row >= N) row = N - 1;  // partial tile: duplicate a valid row, discarded below
+    wp[t] = base + (size_t)row * K + 8 * grp;
+  }
+  const uint16_t* xp[MT];
+  bool xv[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t r = m0 + 16 * m + col;
+    xv[m] = r < M;
+    xp[m] = X + (size_t)(xv[m] ? r : 0) * K + 8 * grp;
+  }
+
+  v4f acc[TPW][MT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = K / 32;
+  uint4 a_cur[TPW], a_nxt[TPW], b_cur[MT], b_nxt[MT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) a_cur[t] = *reinterpret_cast<const uint4*>(wp[t]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    b_cur[m] = xv[m] ? *reinterpret_cast<const uint4*>(xp[m]) : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < steps; ++s) {
+    if (s + 1 < steps) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        a_nxt[t] = *reinterpret_cast<const uint4*>(wp[t] + (size_t)(s + 1) * 32);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        b_nxt[m] = xv[m] ? *reinterpret_cast<const uint4*>(xp[m] + (size_t)(s + 1) * 32)
+                         : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[t][m] = mfma_bf16(a_cur[t], b_cur[m], acc[t][m]);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) a_cur[t] = a_nxt[t];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) b_cur[m] = b_nxt[m];
+  }
+
+  // D layout: lane l holds D[4*(l/16)+v][l%16] = C[token l%16][row 4*(l/16)+v]
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t r = m0 + 16 * m + col;
+    if (r >= M) continue;
+    if (EPI == EPI_F32) {
+      float* o = static_cast<float*>(out) + (size_t)r * N;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int c = n0 + 16 * t + 4 * grp;
+        if ((N & 3) == 0) {
+          if (c < N)
+            *reinterpret_cast<float4*>(o + c) =
+                make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (c + v < N) o[c + v] = acc[t][m][v];
+        }
+      }
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)r * N;
+#pragma unroll
+      for (int t = 0; t < TPW / 2; ++t) {
+        const int c = n0 + 16 * t + 4 * grp;
+        uint32_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g = fminf(fmaxf(acc[t][m][v], -limit), limit);
+          const float u = fminf(fmaxf(acc[t + TPW / 2][m][v], -limit), limit);
+          hv[v] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        }
+        if (c < N) *reinterpret_cast<uint2*>(o + c) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
+    }
+  }
+}
+
+template <int EPI, int TPW>
+static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* W3, void* out,
+                              int64_t M, int N, int K, float limit, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  constexpr int WROWS = EPI == EPI_SWIGLU ? 8 * TPW : 16 * TPW;
+  const unsigned gx = (unsigned)((N + 4 * WROWS - 1) / (4 * WROWS));
+  if (M <= 16) {
+    hipLaunchKernelGGL((bf16_gemm_kernel<EPI, TPW, 1>), dim3(gx, (unsigned)((M + 15) / 16)),
+                       dim3(256), 0, st, X, W, W3, out, M, N, K, limit);
+  } else {
+    hipLaunchKernelGGL((bf16_gemm_kernel<EPI, TPW, 4>), dim3(gx, (unsigned)((M + 63) / 64)),
+                       dim3(256), 0, st, X, W, W3, out, M, N, K, limit);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
+                              int H, int E, hipStream_t st) {
+  return launch_bf16<EPI_F32, 1>(x, wg, nullptr, logits, T, E, H, 0.f, st);
+}
+
+hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                            uint16_t* h, int64_t T, int H, int I, float limit, hipStream_t st) {
+  return launch_bf16<EPI_SWIGLU, 2>(x, w1, w3, h, T, I, H, limit, st);
+}
+
+hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, int64_t T,
+                              int H, int I, hipStream_t st) {
+  return launch_bf16<EPI_F32, 1>(h, w2, nullptr, ysh, T, H, I, 0.f, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+// Internal declarations shared by the HIP sources of the library: kernel
+// launchers (host functions, one per kernel family) and small device helpers.
+// Nothing here is part of the public C ABI (include/moe_fp4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Smallest integer e with a <= 448 * 2^e for a finite a >= 0, clamped to
+// [-127, 127]; a == 0 (and any a below 2^-126) gives -127.  Exact: with
+// a = 1.m * 2^(E-127), 448 = 1.75 * 2^8, so e = E - 135 when the mantissa is
+// at most 0.75 (0x600000) and E - 134 otherwise.
+__device__ __forceinline__ int pow2_scale_exp(float a) {
+  uint32_t u = __float_as_uint(a);
+  int E = (int)(u >> 23);
+  if (E == 0) return -127;
+  int e = ((u & 0x7FFFFFu) <= 0x600000u) ? E - 135 : E - 134;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E4M3FN code of s, |s| <= 448, round to nearest even, sign kept (software).
+__device__ __forceinline__ uint32_t e4m3_rne(float s) {
+  uint32_t u = __float_as_uint(s);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {               // |s| >= 2^-6: normal E4M3 range
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);             // rebias 127 -> 7
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {                              // subnormal step 2^-9
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------------------
+// Tiling constants of the grouped expert GEMMs
+// ---------------------------------------------------------------------------
+constexpr int kGemmThreads = 256;     // 4 waves
+constexpr int kG1Cols = 128;          // h columns per GEMM1 workgroup (one FP8 block)
+constexpr int kG2Rows = 256;          // output columns per GEMM2 workgroup
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipGetLastError() after enqueueing)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* q,
+                            uint8_t* scale, hipStream_t st);
+
+// logits[t, e] = sum_h x[t, h] * wg[e, h]  (bf16 in, fp32 out)
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
+                              int H, int E, hipStream_t st);
+
+hipError_t launch_score_topk(const float* logits, const float* bias, int64_t T, int E, int k,
+                             float route_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);
+
+hipError_t launch_hash_route(const int64_t* token_ids, int64_t T, int E, int k,
+                             float route_scale, uint64_t seed, int32_t* topk_idx, float* topk_w,
+                             hipStream_t st);
+
+// Stable counting sort of the P = T*k pairs by expert.
+size_t permute_scratch_bytes(int64_t P, int E);
+hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* expert_offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, void* scratch,
+                          hipStream_t st);
+
+// Tile prefix of the grouped GEMMs: mtile_off[e] = sum_{e'<e} ceil(n_e'/bm).
+hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int32_t* mtile_off,
+                              hipStream_t st);
+
+struct ExpertGemmArgs {
+  const uint8_t* a;          // FP8 rows: xq [T, K] (GEMM1) or hq [P, K] (GEMM2)
+  const uint8_t* a_scale;    // [rows, K/128]
+  const uint8_t* w;          // GEMM1: w1; GEMM2: w2
+  const uint8_t* w_scale;
+  const uint8_t* w3;         // GEMM1 only
+  const uint8_t* w3_scale;
+  const int32_t* expert_offsets;
+  const int32_t* sorted_pairs;
+  const int32_t* mtile_off;
+  int E, K, N, top_k;        // N = I (GEMM1) or H (GEMM2); K = H or I
+  int64_t P;
+  float limit;               // GEMM1: SwiGLU clamp
+  uint8_t* hq;               // GEMM1 out
+  uint8_t* hs;
+  void* out;                 // GEMM2 out
+  int out_fp32;
+};
+
+// bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
+hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+
+// Shared expert (bf16): h = bf16(clamped_swiglu(x w1^T, x w3^T)) [T, I];
+// ysh = h w2^T [T, H] fp32.
+hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                            uint16_t* h, int64_t T, int H, int I, float limit, hipStream_t st);
+hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, int64_t T,
+                              int H, int I, hipStream_t st);
+
+// y[t] = bf16(sum_j w[t,j] * o[pair_pos[t*k+j]] + ysh[t]); o fp32 [P, H].
+hipError_t launch_combine(const float* o, const float* topk_w, const int32_t* pair_pos,
+                          const float* ysh, uint16_t* y, int64_t T, int H, int k,
+                          hipStream_t st);
+
+}  // namespace moe

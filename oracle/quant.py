@@ -65,10 +65,14 @@ def act_quant(v, block=ACT_BLOCK):
     return codes, (e + 127).astype(np.uint8)
 
 
+_E4M3_TABLE = formats.e4m3_decode(np.arange(256))
+_E2M1_TABLE = formats.e2m1_table()
+
+
 def act_dequant(codes, scales, block=ACT_BLOCK):
     codes = np.asarray(codes)
     rows, cols = codes.shape
-    val = formats.e4m3_decode(codes).reshape(rows, cols // block, block)
+    val = _E4M3_TABLE[codes].reshape(rows, cols // block, block)
     sc = formats.e8m0_decode(scales)[:, :, None]
     return (val * sc).reshape(rows, cols)
 
@@ -88,7 +92,7 @@ def mxfp4_dequant(packed, scales, block=W_BLOCK):
     codes = unpack_nibbles(packed)
     n, k = codes.shape
     assert scales.shape == (n, k // block)
-    val = formats.e2m1_decode(codes).reshape(n, k // block, block)
+    val = _E2M1_TABLE[codes].reshape(n, k // block, block)
     return (val * formats.e8m0_decode(scales)[:, :, None]).reshape(n, k)
 
 
