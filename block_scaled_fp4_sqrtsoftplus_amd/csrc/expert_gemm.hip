@@ -24,6 +24,14 @@
 // So one K step is 128 elements: 64 weight bytes and 128 activation bytes
 // per row, and the FP8 activation block scale lines up with the step.
 //
+// Scale operands: the instruction reads its per-lane E8M0 scale registers
+// over several cycles after issue (measured: a scale register rewritten by
+// the very next VALU instruction gave rows 1-15 of the 16x16 tile the new
+// value, row 0 the old one), and the compiler neither holds such writes back
+// nor keeps a scale register untouched after its last use.  So the
+// instruction is issued from inline assembly followed by 32 wait states
+// (mfma_fp4_fp8 below); the scale bytes are loaded per lane.
+//
 // Work decomposition: a workgroup (4 waves) owns one m-tile of one expert
 // (16 * MT pairs) and one n-tile of weight rows; it streams its weight rows
 // once over the whole K with 16-byte loads straight into the MFMA operand
@@ -36,17 +44,33 @@
 // together there, and share that XCD's L2.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// acc += (A * 2^(sa-127)) x (B * 2^(sb-127)) per 32-element K block; A is 32
+// FP4 values per lane (cbsz 4), B 32 FP8 values per lane (blgp 0), scale
+// bytes in bits 0-7 of sa / sb (op_sel 0).  Issued from inline assembly so
+// that the 32 wait states after it are guaranteed: no instruction of this
+// wave can overwrite a scale (or data) register the instruction may still be
+// reading, and its result is final before any later VALU read.
 __device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& b0, const uint4& b1,
                                             v4f acc, int sa, int sb) {
-  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v4i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
   v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
             (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 0, 0, sa, 0, sb);
+  asm volatile(
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : "+v"(acc)
+      : "v"(av), "v"(bv), "v"(sa), "v"(sb));
+  return acc;
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -79,7 +103,8 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
                                                                     int n_tiles) {
   constexpr int BM = 16 * MT;
   constexpr int LDS_ROW = 144;  // 128 activation bytes + 16 pad (bank spread)
-  __shared__ __attribute__((aligned(16))) uint8_t bsm[MT > 1 ? 2 : 1][MT > 1 ? BM : 1][LDS_ROW];
+  constexpr bool STAGED = MT > 1;
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[STAGED ? 2 : 1][STAGED ? BM : 1][LDS_ROW];
   __shared__ float red[4][BM];
 
   int n_tile, e, m0, off_e, n_e;
@@ -90,7 +115,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
   const int col = lane & 15;   // token slot within a 16-column sub-tile
   const int grp = lane >> 4;   // K group
   const int K = p.K, N = p.N;
-  const int steps = K / 128;
+  const int S = K / 128;
   const size_t wrow_bytes = (size_t)K / 2;
   const size_t srow_bytes = (size_t)K / 32;
 
@@ -107,7 +132,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
       wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp;
     }
   } else {
     n0 = n_tile * kG2Rows;
@@ -116,24 +141,31 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
     for (int t = 0; t < 4; ++t) {
       const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
       wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp;
     }
   }
 
-  // ---- activation rows of the MT sub-tiles (this lane's token column) ----
+  // ---- activation rows (this lane's token column in each sub-tile); slots
+  // past the expert's last pair read that last pair's row, results dropped
+  auto act_row = [&](int slot) -> int64_t {
+    slot = min(slot, n_e - 1);
+    return (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k) : (int64_t)(off_e + slot);
+  };
   const uint8_t* bptr[MT];
   const uint8_t* bsp[MT];
-  bool bval[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int slot = m0 + 16 * m + col;
-    bval[m] = slot < n_e;
-    int64_t row = 0;
-    if (bval[m]) row = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
-                                   : (int64_t)(off_e + slot);
-    bptr[m] = p.a + row * K;
+    const int64_t row = act_row(m0 + 16 * m + col);
+    bptr[m] = p.a + row * K + 16 * grp;
     bsp[m] = p.a_scale + row * (K / 128);
   }
+  // LDS staging (MT > 1): thread i copies 16 bytes of token row i/8 (+32)
+  constexpr int ST_ROUNDS = STAGED ? (BM * 8) / kGemmThreads : 1;
+  const uint8_t* st_src[ST_ROUNDS];
+  const int st_chunk = threadIdx.x & 7;
+#pragma unroll
+  for (int r = 0; r < ST_ROUNDS; ++r)
+    st_src[r] = p.a + act_row(m0 + (threadIdx.x >> 3) + 32 * r) * K + 16 * st_chunk;
 
   v4f acc[4][MT];
 #pragma unroll
@@ -141,127 +173,81 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // staging loader for MT > 1: thread i copies 16 bytes of one token row
-  int st_tok[MT > 1 ? 2 : 1], st_chunk = threadIdx.x & 7;
-  const uint8_t* st_src[MT > 1 ? 2 : 1];
-  bool st_val[MT > 1 ? 2 : 1];
-  if constexpr (MT > 1) {
+  // Two-stage register ring, unrolled so that no register is ever copied:
+  // stage X holds one K step's weight bytes, scale bytes and (unstaged)
+  // activation bytes, all written by loads only.
+  struct Stage {
+    uint4 a[4];
+    uint32_t sa[4];
+    uint4 b[MT][2];
+    uint32_t sb[MT];
+    uint4 st[ST_ROUNDS];
+  };
+  Stage X0, X1;
+  auto load = [&](int s, Stage& x) {
+    if (wave_live) {
 #pragma unroll
-    for (int r = 0; r < (BM * 8 + kGemmThreads - 1) / kGemmThreads && r < 2; ++r) {
-      const int tok = (threadIdx.x >> 3) + 32 * r;
-      st_tok[r] = tok;
-      const int slot = m0 + tok;
-      st_val[r] = tok < BM && slot < n_e;
-      int64_t row = 0;
-      if (st_val[r]) row = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
-                                       : (int64_t)(off_e + slot);
-      st_src[r] = p.a + row * K + 16 * st_chunk;
+      for (int t = 0; t < 4; ++t) {
+        x.a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
+        x.sa[t] = sptr[t][(size_t)s * 4];
+      }
     }
-  }
-  constexpr int ST_ROUNDS = MT > 1 ? ((BM * 8 + kGemmThreads - 1) / kGemmThreads) : 0;
-
-  if (wave_live || MT > 1) {
-    uint4 a_cur[4], a_nxt[4];
-    uint32_t s_cur[4], s_nxt[4];
-    uint4 b_cur[MT][2], b_nxt[MT][2];
-    int bs_cur[MT], bs_nxt[MT];
-    uint4 st_reg[2];
-
-    auto load_a = [&](int s, uint4* a, uint32_t* sc) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-        sc[t] = *reinterpret_cast<const uint32_t*>(sptr[t] + (size_t)s * 4);
+    for (int m = 0; m < MT; ++m) {
+      x.sb[m] = bsp[m][s];
+      if constexpr (!STAGED) {
+        x.b[m][0] = *reinterpret_cast<const uint4*>(bptr[m] + (size_t)s * 128);
+        x.b[m][1] = *reinterpret_cast<const uint4*>(bptr[m] + (size_t)s * 128 + 64);
       }
-    };
-    auto load_b_direct = [&](int s, uint4 (*b)[2], int* bs) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (bval[m]) {
-          b[m][0] = *reinterpret_cast<const uint4*>(bptr[m] + (size_t)s * 128 + 16 * grp);
-          b[m][1] = *reinterpret_cast<const uint4*>(bptr[m] + (size_t)s * 128 + 64 + 16 * grp);
-          bs[m] = bsp[m][s];
-        } else {
-          b[m][0] = make_uint4(0, 0, 0, 0);
-          b[m][1] = make_uint4(0, 0, 0, 0);
-          bs[m] = 127;
-        }
-      }
-    };
-    auto load_bs = [&](int s, int* bs) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) bs[m] = bval[m] ? (int)bsp[m][s] : 127;
-    };
-    auto stage_load = [&](int s) {
+    }
+    if constexpr (STAGED) {
 #pragma unroll
       for (int r = 0; r < ST_ROUNDS; ++r)
-        st_reg[r] = st_val[r] ? *reinterpret_cast<const uint4*>(st_src[r] + (size_t)s * 128)
-                              : make_uint4(0, 0, 0, 0);
-    };
-    auto stage_store = [&](int buf) {
+        x.st[r] = *reinterpret_cast<const uint4*>(st_src[r] + (size_t)s * 128);
+    }
+  };
+  auto stage_store = [&](int buf, const Stage& x) {
 #pragma unroll
-      for (int r = 0; r < ST_ROUNDS; ++r)
-        if (st_tok[r] < BM)
-          *reinterpret_cast<uint4*>(&bsm[buf][st_tok[r]][16 * st_chunk]) = st_reg[r];
-    };
-    auto read_b_lds = [&](int buf, uint4 (*b)[2]) {
+    for (int r = 0; r < ST_ROUNDS; ++r)
+      *reinterpret_cast<uint4*>(&bsm[buf][(threadIdx.x >> 3) + 32 * r][16 * st_chunk]) = x.st[r];
+  };
+  auto compute = [&](int buf, Stage& x) {
+    if constexpr (STAGED) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        b[m][0] = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][16 * grp]);
-        b[m][1] = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][64 + 16 * grp]);
+        x.b[m][0] = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][16 * grp]);
+        x.b[m][1] = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][64 + 16 * grp]);
       }
-    };
-    auto compute = [&](const uint4* a, const uint32_t* sc, uint4 (*b)[2], const int* bs) {
+    }
+    if (wave_live) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int sa = (int)((sc[t] >> (8 * grp)) & 0xFFu);
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          acc[t][m] = mfma_fp4_fp8(a[t], b[m][0], b[m][1], acc[t][m], sa, bs[m]);
-      }
-    };
-
-    if constexpr (MT == 1) {
-      load_a(0, a_cur, s_cur);
-      load_b_direct(0, b_cur, bs_cur);
-      for (int s = 0; s < steps; ++s) {
-        if (s + 1 < steps) {
-          load_a(s + 1, a_nxt, s_nxt);
-          load_b_direct(s + 1, b_nxt, bs_nxt);
-        }
-        compute(a_cur, s_cur, b_cur, bs_cur);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { a_cur[t] = a_nxt[t]; s_cur[t] = s_nxt[t]; }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          b_cur[m][0] = b_nxt[m][0]; b_cur[m][1] = b_nxt[m][1]; bs_cur[m] = bs_nxt[m];
-        }
-      }
-    } else {
-      stage_load(0);
-      stage_store(0);
-      if (wave_live) load_a(0, a_cur, s_cur);
-      load_bs(0, bs_cur);
-      __syncthreads();
-      for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < steps) {
-          stage_load(s + 1);
-          if (wave_live) load_a(s + 1, a_nxt, s_nxt);
-          load_bs(s + 1, bs_nxt);
-        }
-        if (wave_live) {
-          read_b_lds(buf, b_cur);
-          compute(a_cur, s_cur, b_cur, bs_cur);
-        }
-        if (s + 1 < steps) stage_store(buf ^ 1);
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { a_cur[t] = a_nxt[t]; s_cur[t] = s_nxt[t]; }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) bs_cur[m] = bs_nxt[m];
-      }
+          acc[t][m] = mfma_fp4_fp8(x.a[t], x.b[m][0], x.b[m][1], acc[t][m], (int)x.sa[t], (int)x.sb[m]);
     }
+  };
+  // one K step: compute from x (its activations in LDS buffer `buf` when
+  // staged), then refill x with step s + 2 (clamped to the last step, whose
+  // reload is harmless) and stage step s + 1 for the next round
+  auto step = [&](int s, int buf, Stage& x, Stage& other) {
+    compute(buf, x);
+    if constexpr (STAGED) {
+      if (s + 1 < S) stage_store(buf ^ 1, other);
+      __syncthreads();
+    }
+    load(min(s + 2, S - 1), x);
+  };
+
+  load(0, X0);
+  load(min(1, S - 1), X1);
+  if constexpr (STAGED) {
+    stage_store(0, X0);
+    __syncthreads();
+  }
+  for (int s = 0; s < S; s += 2) {
+    step(s, 0, X0, X1);
+    if (s + 1 < S) step(s + 1, 1, X1, X0);
   }
 
   if (MODE == 1) {
@@ -328,6 +314,148 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant for m-tiles of at most 16 pairs (decode) when K is a
+// multiple of 512: every wave keeps four K steps of weight, activation and
+// scale loads in flight in a register ring (no register copies, no branches
+// around the loads, so the waits before each step's MFMAs cover only that
+// step).  Lanes whose pair slot lies past the expert's last pair read that
+// last pair's row: their columns are computed and dropped.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArgs p, int mt_max,
+                                                                    int n_tiles) {
+  __shared__ float red[4][16];
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int S = K / 128;                    // multiple of 4
+  const size_t wrow_bytes = (size_t)K / 2;
+  const size_t srow_bytes = (size_t)K / 32;
+
+  const uint8_t* wptr[4];
+  const uint8_t* sptr[4];
+  int n0;
+  bool wave_live = true;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const uint8_t* base = (t < 2) ? p.w : p.w3;
+      const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
+      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp;
+    }
+  } else {
+    n0 = n_tile * kG2Rows;
+    wave_live = (n0 + 64 * wv) < N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
+      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp;
+    }
+  }
+  const int slot = min(m0 + col, n_e - 1);
+  const int64_t brow = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
+                                   : (int64_t)(off_e + slot);
+  const uint8_t* bptr = p.a + brow * K + 16 * grp;
+  const uint8_t* bsp = p.a_scale + brow * (K / 128);
+
+  v4f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (wave_live) {
+    // Ring of four K steps: weight bytes, activation bytes and the E8M0
+    // scale bytes of each, all written only by loads (see the note on
+    // scale operands at the top of this file).
+    uint4 A[4][4], B[4][2];
+    uint32_t SA[4][4], SB[4];
+    auto load_step = [&](int s, uint4 (&a)[4], uint4 (&b)[2], uint32_t (&sa)[4], uint32_t& sb) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
+        sa[t] = sptr[t][(size_t)s * 4];
+      }
+      b[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
+      b[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
+      sb = bsp[s];
+    };
+    auto four_steps = [&](auto loads, int s0) {
+      constexpr bool LOADS = decltype(loads)::value;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t] = mfma_fp4_fp8(A[d][t], B[d][0], B[d][1], acc[t], (int)SA[d][t], (int)SB[d]);
+        if constexpr (LOADS) load_step(s0 + d + 4, A[d], B[d], SA[d], SB[d]);
+      }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) load_step(d, A[d], B[d], SA[d], SB[d]);
+    for (int s0 = 0; s0 < S - 4; s0 += 4) four_steps(yes{}, s0);
+    four_steps(no{}, S - 4);
+  }
+
+  if (MODE == 1) {
+    float h[2][4];
+    const float lim = p.limit;
+    float amax = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
+        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
+        const float hv = silu_f(g) * u;
+        h[tt][v] = hv;
+        amax = fmaxf(amax, fabsf(hv));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (lane < 16) red[wv][lane] = amax;
+    __syncthreads();
+    const float bmax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+    const int ex = pow2_scale_exp(bmax);
+    if (m0 + col < n_e) {
+      const size_t row = (size_t)(off_e + m0 + col);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[tt][v], -ex)) << (8 * v);
+        *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
+      }
+      if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+    }
+  } else {
+    if (!wave_live || m0 + col >= n_e) return;
+    const size_t row = (size_t)(off_e + m0 + col);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
+      if (p.out_fp32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
+            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+      } else {
+        const uint32_t lo = f32_to_bf16(acc[t][0]) | (f32_to_bf16(acc[t][1]) << 16);
+        const uint32_t hi = f32_to_bf16(acc[t][2]) | (f32_to_bf16(acc[t][3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
+            make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
 static inline unsigned pad8(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
 
 template <int MODE>
@@ -335,7 +463,10 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (bm == 16) {
+  if (bm == 16 && a.K % 512 == 0) {
+    hipLaunchKernelGGL((expert_gemm_stream<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
+  } else if (bm == 16) {
     hipLaunchKernelGGL((expert_gemm_kernel<MODE, 1>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   } else {
