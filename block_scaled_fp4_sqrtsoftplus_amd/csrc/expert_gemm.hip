@@ -30,7 +30,7 @@
 // value, row 0 the old one), and the compiler neither holds such writes back
 // nor keeps a scale register untouched after its last use.  So the
 // instruction is issued from inline assembly followed by 32 wait states
-// (mfma_fp4_fp8 below); the scale bytes are loaded per lane.
+// (mfma_fp4_fp8 below), after which scale registers may be reused freely.
 //
 // Work decomposition: a workgroup (4 waves) owns one m-tile of one expert
 // (16 * MT pairs) and one n-tile of weight rows; it streams its weight rows
@@ -316,10 +316,10 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
 
 // ---------------------------------------------------------------------------
 // Streaming variant for m-tiles of at most 16 pairs (decode) when K is a
-// multiple of 512: every wave keeps four K steps of weight, activation and
-// scale loads in flight in a register ring (no register copies, no branches
+// multiple of 1024: every wave keeps four K steps of weight and activation
+// loads in flight in a register ring (no register copies, no branches
 // around the loads, so the waits before each step's MFMAs cover only that
-// step).  Lanes whose pair slot lies past the expert's last pair read that
+// step), and reads scales 16 / 4 bytes at a time, once per four steps.  Lanes whose pair slot lies past the expert's last pair read that
 // last pair's row: their columns are computed and dropped.
 // ---------------------------------------------------------------------------
 template <int MODE>
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int K = p.K, N = p.N;
-  const int S = K / 128;                    // multiple of 4
+  const int S = K / 128;                    // multiple of 8
   const size_t wrow_bytes = (size_t)K / 2;
   const size_t srow_bytes = (size_t)K / 32;
 
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
       wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes;
     }
   } else {
     n0 = n_tile * kG2Rows;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
     for (int t = 0; t < 4; ++t) {
       const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
       wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
     }
   }
   const int slot = min(m0 + col, n_e - 1);
@@ -373,37 +373,63 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   if (wave_live) {
-    // Ring of four K steps: weight bytes, activation bytes and the E8M0
-    // scale bytes of each, all written only by loads (see the note on
-    // scale operands at the top of this file).
+    // Ring of four K steps of weight and activation bytes, plus the scale
+    // bytes of the current and the next four-step group (one 16-byte load
+    // per weight tile: the row's 16 per-32 scales of 4 steps; one 4-byte
+    // load of the token's 4 per-128 activation scales).
     uint4 A[4][4], B[4][2];
-    uint32_t SA[4][4], SB[4];
-    auto load_step = [&](int s, uint4 (&a)[4], uint4 (&b)[2], uint32_t (&sa)[4], uint32_t& sb) {
+    uint4 SA0[4], SA1[4];
+    uint32_t SB0, SB1;
+    auto load_step = [&](int s, uint4 (&a)[4], uint4 (&b)[2]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-        sa[t] = sptr[t][(size_t)s * 4];
-      }
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
       b[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
       b[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
-      sb = bsp[s];
     };
-    auto four_steps = [&](auto loads, int s0) {
+    auto load_scales = [&](int q, uint4 (&sa)[4], uint32_t& sb) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sa[t] = *reinterpret_cast<const uint4*>(sptr[t] + (size_t)q * 16);
+      sb = *reinterpret_cast<const uint32_t*>(bsp + (size_t)q * 4);
+    };
+    // four K steps (group q); with LOADS also the next group's scales and a
+    // refill of each ring slot right after its use.  The loads of one step
+    // are issued as a group, in step order, in the prologue and here
+    // (scheduling barriers keep the compiler from regrouping them), so the
+    // wait before a step's MFMAs leaves the three later steps in flight.
+    auto four_steps = [&](auto loads, int q, const uint4 (&sac)[4], uint32_t sbc,
+                          uint4 (&san)[4], uint32_t& sbn) {
       constexpr bool LOADS = decltype(loads)::value;
+      if constexpr (LOADS) load_scales(q + 1, san, sbn);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        const int sb = (int)(sbc >> (8 * d));          // the MFMA reads bits 0-7
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[t] = mfma_fp4_fp8(A[d][t], B[d][0], B[d][1], acc[t], (int)SA[d][t], (int)SB[d]);
-        if constexpr (LOADS) load_step(s0 + d + 4, A[d], B[d], SA[d], SB[d]);
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = d == 0 ? sac[t].x : d == 1 ? sac[t].y : d == 2 ? sac[t].z : sac[t].w;
+          acc[t] = mfma_fp4_fp8(A[d][t], B[d][0], B[d][1], acc[t], (int)(w >> (8 * grp)), sb);
+        }
+        if constexpr (LOADS) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_step(4 * q + d + 4, A[d], B[d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
+    load_scales(0, SA0, SB0);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) load_step(d, A[d], B[d], SA[d], SB[d]);
-    for (int s0 = 0; s0 < S - 4; s0 += 4) four_steps(yes{}, s0);
-    four_steps(no{}, S - 4);
+    for (int d = 0; d < 4; ++d) {
+      load_step(d, A[d], B[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int Q = S / 4;  // even, >= 2
+    for (int q = 0; q < Q - 2; q += 2) {
+      four_steps(yes{}, q, SA0, SB0, SA1, SB1);
+      four_steps(yes{}, q + 1, SA1, SB1, SA0, SB0);
+    }
+    four_steps(yes{}, Q - 2, SA0, SB0, SA1, SB1);
+    four_steps(no{}, Q - 1, SA1, SB1, SA0, SB0);
   }
 
   if (MODE == 1) {
@@ -463,7 +489,7 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (bm == 16 && a.K % 512 == 0) {
+  if (bm == 16 && a.K % 1024 == 0) {
     hipLaunchKernelGGL((expert_gemm_stream<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   } else if (bm == 16) {
