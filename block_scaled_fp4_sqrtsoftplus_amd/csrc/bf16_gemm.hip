@@ -14,6 +14,8 @@
 //              columns; out[t][n] = bf16(silu(clip(g)) * clip(u))
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -138,10 +140,153 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const uint16_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-sized variant (M <= 64 tokens, K a multiple of 1024): the weights
+// are the whole traffic, so parallelism comes from splitting K.  A
+// workgroup of 8 waves owns 16 weight rows (EPI_F32) or 16 h columns, i.e.
+// one w1 tile and one w3 tile (EPI_SWIGLU), and all M tokens; wave w streams
+// the K slice [w K/8, (w+1) K/8) with a four-step register ring, and the
+// eight partial sums are added in LDS in a fixed order (a three-level tree),
+// so results do not depend on timing.
+// ---------------------------------------------------------------------------
+template <int EPI, int MT>
+__global__ __launch_bounds__(512) void bf16_skinny_kernel(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ W,
+                                                          const uint16_t* __restrict__ W3,
+                                                          void* __restrict__ out, int M, int N,
+                                                          int K, float limit) {
+  constexpr int NT = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr int NACC = NT * MT * 4;
+  __shared__ float red[4][NACC][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int KW = K / 8;
+  const int k0 = wv * KW;
+  const int steps = KW / 32;  // multiple of 4
+
+  const uint16_t* wp[NT];
+  const int row = min(n0 + col, N - 1);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wp[t] = (t == 0 ? W : W3) + (size_t)row * K + k0 + 8 * grp;
+  const uint16_t* xp[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xp[m] = X + (size_t)min(16 * m + col, M - 1) * K + k0 + 8 * grp;
+
+  v4f acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 A[4][NT], B[4][MT];
+  auto load = [&](int s, uint4 (&a)[NT], uint4 (&b)[MT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a[t] = *reinterpret_cast<const uint4*>(wp[t] + (size_t)s * 32);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) b[m] = *reinterpret_cast<const uint4*>(xp[m] + (size_t)s * 32);
+  };
+  auto four = [&](auto loads, int s0) {
+    constexpr bool LOADS = decltype(loads)::value;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[t][m] = mfma_bf16(A[d][t], B[d][m], acc[t][m]);
+      if constexpr (LOADS) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(s0 + d + 4, A[d], B[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    load(d, A[d], B[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int s0 = 0; s0 < steps - 4; s0 += 4) four(yes{}, s0);
+  four(no{}, steps - 4);
+
+  // deterministic tree: 8 -> 4 -> 2 -> 1 partial sums
+  auto put = [&](int slot) {
+    int i = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[slot][i++][lane] = acc[t][m][v];
+  };
+  auto add = [&](int slot) {
+    int i = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][m][v] += red[slot][i++][lane];
+  };
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (wv >= half && wv < 2 * half) put(wv - half);
+    __syncthreads();
+    if (wv < half) add(wv);
+    __syncthreads();
+  }
+  if (wv != 0) return;
+
+  // D layout: lane l holds D[4*(l/16)+v][l%16] = C[token l%16][row 4*(l/16)+v]
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int r = 16 * m + col;
+    if (r >= M) continue;
+    const int c = n0 + 4 * grp;
+    if (EPI == EPI_F32) {
+      float* o = static_cast<float*>(out) + (size_t)r * N;
+      if ((N & 3) == 0) {
+        if (c < N) *reinterpret_cast<float4*>(o + c) = make_float4(acc[0][m][0], acc[0][m][1], acc[0][m][2], acc[0][m][3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (c + v < N) o[c + v] = acc[0][m][v];
+      }
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)r * N;
+      uint32_t hv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = fminf(fmaxf(acc[0][m][v], -limit), limit);
+        const float u = fminf(fmaxf(acc[1][m][v], -limit), limit);
+        hv[v] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+      }
+      if (c < N) *reinterpret_cast<uint2*>(o + c) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    }
+  }
+}
+
+template <int EPI>
+static hipError_t launch_skinny(const uint16_t* X, const uint16_t* W, const uint16_t* W3, void* out,
+                                int M, int N, int K, float limit, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 15) / 16));
+  switch ((M + 15) / 16) {
+    case 1: hipLaunchKernelGGL((bf16_skinny_kernel<EPI, 1>), grid, dim3(512), 0, st, X, W, W3, out, M, N, K, limit); break;
+    case 2: hipLaunchKernelGGL((bf16_skinny_kernel<EPI, 2>), grid, dim3(512), 0, st, X, W, W3, out, M, N, K, limit); break;
+    case 3: hipLaunchKernelGGL((bf16_skinny_kernel<EPI, 3>), grid, dim3(512), 0, st, X, W, W3, out, M, N, K, limit); break;
+    default: hipLaunchKernelGGL((bf16_skinny_kernel<EPI, 4>), grid, dim3(512), 0, st, X, W, W3, out, M, N, K, limit); break;
+  }
+  return hipGetLastError();
+}
+
 template <int EPI, int TPW>
 static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* W3, void* out,
                               int64_t M, int N, int K, float limit, hipStream_t st) {
   if (M == 0) return hipSuccess;
+  if (M <= 64 && K % 1024 == 0) return launch_skinny<EPI>(X, W, W3, out, (int)M, N, K, limit, st);
   constexpr int WROWS = EPI == EPI_SWIGLU ? 8 * TPW : 16 * TPW;
   const unsigned gx = (unsigned)((N + 4 * WROWS - 1) / (4 * WROWS));
   if (M <= 16) {

@@ -271,3 +271,19 @@ def test_expert_ffn_unclamped_limit():
     hq, hs = host(g["hq"]), host(g["hs"])
     _check_hq(hq, hs, ref, dh, max_flip_frac=0.02)
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
+
+
+@pytest.mark.parametrize("T,E,H", [(1, 40, 1024), (17, 256, 4096), (37, 33, 2048), (64, 384, 4096)])
+def test_router_logits_small_batches(T, E, H):
+    # the decode-sized router GEMM (K split over 8 waves, LDS tree reduction)
+    wl = synth.WORKLOADS["decode"].replace(n_experts=E, hidden=H)
+    inp = synth.make_inputs(wl, tokens=T, experts_only=[])
+    cfg = config(moe, wl, tokens=T)
+    g = moe.route(cfg, x=dev_bf16(inp["x"]), w_gate=dev_bf16(inp["w_gate"]), want_logits=True)
+    torch.cuda.synchronize()
+    z = host(g["logits"]).astype(np.float64)
+    xa = np.abs(formats.bf16_decode(inp["x"]))
+    wa = np.abs(formats.bf16_decode(inp["w_gate"]))
+    exact = formats.bf16_decode(inp["x"]) @ formats.bf16_decode(inp["w_gate"]).T
+    bound = H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.abs(z - exact) <= bound)
