@@ -315,14 +315,14 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
 }
 
 // ---------------------------------------------------------------------------
-// Streaming variant for m-tiles of at most 16 pairs (decode) when K is a
-// multiple of 1024: every wave keeps four K steps of weight and activation
-// loads in flight in a register ring (no register copies, no branches
-// around the loads, so the waits before each step's MFMAs cover only that
-// step), and reads scales 16 / 4 bytes at a time, once per four steps.  Lanes whose pair slot lies past the expert's last pair read that
+// Streaming variant for m-tiles of at most 16 pairs (decode) when K is
+// 1024, 2048 or 4096: every wave keeps four K steps of weight and
+// activation loads in flight in a register ring (no register copies, no
+// branches around the loads, so the waits before each step's MFMAs cover
+// only that step), and reads each weight row's scales once.  Lanes whose pair slot lies past the expert's last pair read that
 // last pair's row: their columns are computed and dropped.
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, int S>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {
   __shared__ float red[4][16];
@@ -333,8 +333,9 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   const int wv = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int K = p.K, N = p.N;
-  const int S = K / 128;                    // multiple of 8
+  constexpr int K = S * 128;                // S in {8, 16, 32}
+  const int N = p.N;
+  constexpr int SD = S / 4;                 // scale dwords per lane group
   const size_t wrow_bytes = (size_t)K / 2;
   const size_t srow_bytes = (size_t)K / 32;
 
@@ -373,63 +374,91 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   if (wave_live) {
-    // Ring of four K steps of weight and activation bytes, plus the scale
-    // bytes of the current and the next four-step group (one 16-byte load
-    // per weight tile: the row's 16 per-32 scales of 4 steps; one 4-byte
-    // load of the token's 4 per-128 activation scales).
+    // Ring of four K steps of weight and activation bytes.  Weight scales:
+    // the four lane groups of a row load the row's whole scale line once (K/32
+    // bytes, a quarter each, back to back), and each step takes its byte from
+    // the lane group holding it with a cross-lane permute.  Activation
+    // scales: one 4-byte load per four steps (4 per-128 scales of the token).
     uint4 A[4][4], B[4][2];
-    uint4 SA0[4], SA1[4];
+    uint32_t SR[4][SD];
     uint32_t SB0, SB1;
-    auto load_step = [&](int s, uint4 (&a)[4], uint4 (&b)[2]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-      b[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
-      b[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
-    };
-    auto load_scales = [&](int q, uint4 (&sa)[4], uint32_t& sb) {
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* src = sptr[t] + grp * S;
+      if constexpr (SD >= 4) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sa[t] = *reinterpret_cast<const uint4*>(sptr[t] + (size_t)q * 16);
-      sb = *reinterpret_cast<const uint32_t*>(bsp + (size_t)q * 4);
+        for (int j = 0; j < SD / 4; ++j) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * j);
+          SR[t][4 * j] = v.x; SR[t][4 * j + 1] = v.y; SR[t][4 * j + 2] = v.z; SR[t][4 * j + 3] = v.w;
+        }
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        SR[t][0] = v.x; SR[t][1] = v.y;
+      }
+    }
+    // steps s and s + 1 (s even) together: the two 64-byte halves of each
+    // weight row's 128-byte line are requested back to back, so the second
+    // request meets the first one's line fill instead of missing again
+    auto load_pair = [&](int s, uint4 (&a0)[4], uint4 (&b0)[2], uint4 (&a1)[4], uint4 (&b1)[2]) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
+        a1[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64 + 64);
+      }
+      b0[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
+      b0[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
+      b1[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 128);
+      b1[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 192);
     };
-    // four K steps (group q); with LOADS also the next group's scales and a
-    // refill of each ring slot right after its use.  The loads of one step
-    // are issued as a group, in step order, in the prologue and here
-    // (scheduling barriers keep the compiler from regrouping them), so the
-    // wait before a step's MFMAs leaves the three later steps in flight.
-    auto four_steps = [&](auto loads, int q, const uint4 (&sac)[4], uint32_t sbc,
-                          uint4 (&san)[4], uint32_t& sbn) {
+    auto load_sb = [&](int q) { return *reinterpret_cast<const uint32_t*>(bsp + (size_t)q * 4); };
+    // four K steps s = 4q + d (q of parity PAR); with LOADS also the next
+    // group's activation scales and a refill of each pair of ring slots right
+    // after their use.  The loads of a step pair are issued as a group, in
+    // step order, in the prologue and here (scheduling barriers keep the
+    // compiler from regrouping them), so the wait before a step's MFMAs
+    // leaves the later steps in flight.
+    auto four_steps = [&](auto loads, auto par, int q, uint32_t sbc, uint32_t& sbn) {
       constexpr bool LOADS = decltype(loads)::value;
-      if constexpr (LOADS) load_scales(q + 1, san, sbn);
+      constexpr int PAR = decltype(par)::value;
+      if constexpr (LOADS) sbn = load_sb(q + 1);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        // byte 4s + grp of the row's scales sits in lane group (4s)/S,
+        // dword s % SD, byte grp
+        const int s = 4 * q + d;
+        const int src_lane = col + 16 * (s / SD);
+        const int dw = (4 * PAR + d) % SD;
         const int sb = (int)(sbc >> (8 * d));          // the MFMA reads bits 0-7
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t w = d == 0 ? sac[t].x : d == 1 ? sac[t].y : d == 2 ? sac[t].z : sac[t].w;
-          acc[t] = mfma_fp4_fp8(A[d][t], B[d][0], B[d][1], acc[t], (int)(w >> (8 * grp)), sb);
+          const int w = __shfl((int)SR[t][dw], src_lane);
+          acc[t] = mfma_fp4_fp8(A[d][t], B[d][0], B[d][1], acc[t], w >> (8 * grp), sb);
         }
         if constexpr (LOADS) {
-          __builtin_amdgcn_sched_barrier(0);
-          load_step(4 * q + d + 4, A[d], B[d]);
-          __builtin_amdgcn_sched_barrier(0);
+          if (d & 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_pair(4 * q + d + 3, A[d - 1], B[d - 1], A[d], B[d]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
-    load_scales(0, SA0, SB0);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      load_step(d, A[d], B[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const int Q = S / 4;  // even, >= 2
+    using even = std::integral_constant<int, 0>;
+    using odd = std::integral_constant<int, 1>;
+    SB0 = load_sb(0);
+    load_pair(0, A[0], B[0], A[1], B[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair(2, A[2], B[2], A[3], B[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int Q = S / 4;  // even, >= 2
     for (int q = 0; q < Q - 2; q += 2) {
-      four_steps(yes{}, q, SA0, SB0, SA1, SB1);
-      four_steps(yes{}, q + 1, SA1, SB1, SA0, SB0);
+      four_steps(yes{}, even{}, q, SB0, SB1);
+      four_steps(yes{}, odd{}, q + 1, SB1, SB0);
     }
-    four_steps(yes{}, Q - 2, SA0, SB0, SA1, SB1);
-    four_steps(no{}, Q - 1, SA1, SB1, SA0, SB0);
+    four_steps(yes{}, even{}, Q - 2, SB0, SB1);
+    four_steps(no{}, odd{}, Q - 1, SB1, SB0);
   }
 
   if (MODE == 1) {
@@ -489,8 +518,14 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (bm == 16 && a.K % 1024 == 0) {
-    hipLaunchKernelGGL((expert_gemm_stream<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+  if (bm == 16 && a.K == 4096) {
+    hipLaunchKernelGGL((expert_gemm_stream<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
+  } else if (bm == 16 && a.K == 2048) {
+    hipLaunchKernelGGL((expert_gemm_stream<MODE, 16>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
+  } else if (bm == 16 && a.K == 1024) {
+    hipLaunchKernelGGL((expert_gemm_stream<MODE, 8>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   } else if (bm == 16) {
     hipLaunchKernelGGL((expert_gemm_kernel<MODE, 1>), dim3(grid), dim3(kGemmThreads), 0, st, a,

@@ -228,6 +228,8 @@ def _check_o(o, hq, hs, ref, r, absw2):
     ("tiny", 37, dict(hidden=512, inter=384, n_experts=12, top_k=3)),
     ("tiny", 200, dict(hidden=256, inter=256, n_experts=8, top_k=2)),      # 50 pairs/expert: 64-token tiles
     ("decode", 8, dict(n_experts=16)),                                      # full H, I
+    ("decode", 10, dict(hidden=1024, inter=1024, n_experts=8)),             # K = 1024 streaming path
+    ("decode", 6, dict(hidden=2048, inter=4096, n_experts=6, top_k=2)),     # K = 2048 / 4096 swapped
     ("tiny", 19, dict(hidden=768, inter=640, n_experts=5, top_k=5, exp_lo=-9, exp_hi=-7)),
 ])
 def test_expert_ffn_parity(shape):
