@@ -54,11 +54,11 @@ def algorithmic(wl, n_touched):
                 flops_routed=flops_routed, flops_shared=flops_shared, flops_router=flops_router)
 
 
-def traffic_record(kernel_src_hash):
+def traffic_record(kernel_src_hash, workload):
     """HBM traffic of the routed expert FFN measured with rocprofv3 --pmc
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel), if the record
-    was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "expert_ffn_decode_traffic.json")
+    was taken on this workload and on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
@@ -184,7 +184,7 @@ def main():
 
     alg = algorithmic(wl, n_touched)
     src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", "expert_gemm.hip"), "rb").read()
-    traffic = traffic_record(hashlib.sha256(src).hexdigest())
+    traffic = traffic_record(hashlib.sha256(src).hexdigest(), wl.name)
     ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
     ffn_tflops = alg["flops_routed"] / (ffn_ms * 1e-3) / 1e12
     hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (MFMA_FP8_PEAK_TFLOPS * 1e12)
