@@ -4,9 +4,11 @@
 // call synchronises or copies to the host.
 #include "moe_fp4.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -51,12 +53,17 @@ struct Carver {
 struct RouteWs {
   int32_t* perm_scratch;
   float* logits;
+  int32_t* mtile_off;  // m-tile prefix written by the single-workgroup routing
 };
 RouteWs carve_route(Carver& cv, const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
   RouteWs r;
   r.perm_scratch = cv.take<int32_t>(permute_scratch_bytes(P, c.n_experts) / sizeof(int32_t) + 1);
-  r.logits = cv.take<float>(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS ? (size_t)c.tokens * c.n_experts : 0);
+  // logits, or their split partial sums for small batches
+  r.logits = cv.take<float>(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS
+                                ? (size_t)c.tokens * c.n_experts * router_splits(c.tokens, c.hidden)
+                                : 0);
+  r.mtile_off = cv.take<int32_t>(c.n_experts + 1);
   return r;
 }
 
@@ -121,6 +128,37 @@ moe_status check_device() {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// One side stream per device (default priority, created on first use and kept
+// for the process) on which moe_layer runs the shared expert, which needs only
+// x.  It forks from and joins back to the caller's stream through two events;
+// the per-device mutex keeps the fork/join pairs of concurrent calls from
+// interleaving.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false;
+};
+SideStream g_side[64];
+
+moe_status side_stream(SideStream*& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  out = &g_side[dev];
+  return MOE_OK;
+}
+
+moe_status side_init_locked(SideStream& s) {
+  if (s.ready) return MOE_OK;
+  if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+  // device-side ordering only: no timing, no system-scope fence on record
+  const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (hipEventCreateWithFlags(&s.fork, flags) != hipSuccess) return MOE_ERR_HIP;
+  if (hipEventCreateWithFlags(&s.join, flags) != hipSuccess) return MOE_ERR_HIP;
+  s.ready = true;
+  return MOE_OK;
+}
+
 #define MOE_TRY(expr)                                   \
   do {                                                  \
     hipError_t _e = (expr);                             \
@@ -152,23 +190,36 @@ int choose_bm(const moe_config& c) {
   return P <= (int64_t)32 * c.n_experts ? 16 : 64;
 }
 
+// Routing (S1-S3).  Small batches run the single-workgroup permutation
+// kernel, which also writes the grouped GEMMs' m-tile prefix to `mtile_off`
+// (when given); the return flag says whether it did.
 moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t* wg,
                          const float* bias, const int64_t* ids, const float* logits_in,
                          float* logits_out, const moe_routing& r, const RouteWs& ws,
-                         hipStream_t st) {
+                         hipStream_t st, int32_t* mtile_off = nullptr, bool* tiles_done = nullptr) {
   const int64_t T = c.tokens, P = T * c.top_k;
+  if (tiles_done) *tiles_done = false;
   if (c.route_mode == MOE_ROUTE_HASH) {
     MOE_TRY(launch_hash_route(ids, T, c.n_experts, c.top_k, c.route_scale, c.hash_seed,
                               r.topk_idx, r.topk_w, st));
+  } else if (logits_in) {
+    MOE_TRY(launch_score_topk(logits_in, 1, logits_out, bias, T, c.n_experts, c.top_k,
+                              c.route_scale, r.topk_idx, r.topk_w, st));
+  } else if (router_splits(T, c.hidden) > 1) {
+    MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, st));
+    MOE_TRY(launch_score_topk(ws.logits, router_splits(T, c.hidden), logits_out, bias, T,
+                              c.n_experts, c.top_k, c.route_scale, r.topk_idx, r.topk_w, st));
   } else {
-    const float* z = logits_in;
-    if (!z) {
-      float* dst = logits_out ? logits_out : ws.logits;
-      MOE_TRY(launch_router_gemm(x, wg, dst, T, c.hidden, c.n_experts, st));
-      z = dst;
-    }
-    MOE_TRY(launch_score_topk(z, bias, T, c.n_experts, c.top_k, c.route_scale, r.topk_idx,
-                              r.topk_w, st));
+    float* dst = logits_out ? logits_out : ws.logits;
+    MOE_TRY(launch_router_gemm(x, wg, dst, T, c.hidden, c.n_experts, st));
+    MOE_TRY(launch_score_topk(dst, 1, nullptr, bias, T, c.n_experts, c.top_k, c.route_scale,
+                              r.topk_idx, r.topk_w, st));
+  }
+  if (P > 0 && P <= kFusedMaxPairs) {
+    MOE_TRY(launch_perm_fused(r.topk_idx, (int)P, c.n_experts, choose_bm(c), r.expert_offsets,
+                              r.sorted_pairs, r.pair_pos, mtile_off ? mtile_off : ws.mtile_off, st));
+    if (tiles_done) *tiles_done = mtile_off != nullptr;
+    return MOE_OK;
   }
   MOE_TRY(launch_permute(r.topk_idx, P, c.n_experts, r.expert_offsets, r.sorted_pairs,
                          r.pair_pos, ws.perm_scratch, st));
@@ -177,13 +228,14 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
 
 moe_status enqueue_ffn(const moe_config& c, const uint8_t* xq, const uint8_t* xs,
                        const moe_routing& r, const moe_expert_weights& w, void* out, int out_fp32,
-                       uint8_t* hq, uint8_t* hs, int32_t* mtile_off, hipStream_t st) {
+                       uint8_t* hq, uint8_t* hs, int32_t* mtile_off, hipStream_t st,
+                       bool tiles_done = false) {
   const int64_t P = c.tokens * c.top_k;
   if (P == 0) return MOE_OK;
   const int bm = choose_bm(c);
   const int64_t mt_max64 = (P + bm - 1) / bm + std::min<int64_t>(c.n_experts, P);
   const int mt_max = (int)mt_max64;
-  MOE_TRY(launch_tile_prefix(r.expert_offsets, c.n_experts, bm, mtile_off, st));
+  if (!tiles_done) MOE_TRY(launch_tile_prefix(r.expert_offsets, c.n_experts, bm, mtile_off, st));
   ExpertGemmArgs a{};
   a.expert_offsets = r.expert_offsets;
   a.sorted_pairs = r.sorted_pairs;
@@ -287,10 +339,6 @@ moe_status moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   Carver cv(ws);
   RouteWs rws = carve_route(cv, c);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (logits_in && logits_out && c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && c.tokens > 0) {
-    MOE_TRY(hipMemcpyAsync(logits_out, logits_in, (size_t)c.tokens * c.n_experts * sizeof(float),
-                           hipMemcpyDeviceToDevice, st));
-  }
   return enqueue_route(c, x, w_gate, bias, token_ids, logits_in, logits_out, *out, rws, st);
 }
 
@@ -358,20 +406,38 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   Carver cv(ws);
   LayerWs l = carve_layer(cv, c);
   const moe_routing& r = routing_out ? *routing_out : l.routing;
-  if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st)) != MOE_OK)
-    return s;
-  if (c.tokens == 0) return MOE_OK;
+  if (c.tokens == 0)
+    return enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st);
+
+  // Caller's stream: quantize x, route, routed experts, combine.  The shared
+  // expert (which needs only x) forks onto the side stream once routing is
+  // enqueued -- so it overlaps the bandwidth-bound expert GEMMs rather than
+  // the latency-bound routing kernels -- and joins before the combine.
   MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
-  if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st)) !=
-      MOE_OK)
+  bool tiles_done = false;
+  if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
+                         l.ffn.mtile_off, &tiles_done)) != MOE_OK)
     return s;
   const float* ysh = nullptr;
+  std::unique_lock<std::mutex> lock;
+  SideStream* side = nullptr;
   if (shared) {
+    if ((s = side_stream(side)) != MOE_OK) return s;
+    lock = std::unique_lock<std::mutex>(side->mu);
+    if ((s = side_init_locked(*side)) != MOE_OK) return s;
+    hipStream_t ss = side->stream;
+    MOE_TRY(hipEventRecord(side->fork, st));
+    MOE_TRY(hipStreamWaitEvent(ss, side->fork, 0));
     MOE_TRY(launch_shared_up(x, shared->w1, shared->w3, l.hsh, c.tokens, c.hidden, c.inter,
-                             c.swiglu_limit, st));
-    MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, c.tokens, c.hidden, c.inter, st));
+                             c.swiglu_limit, ss));
+    MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, c.tokens, c.hidden, c.inter, ss));
+    MOE_TRY(hipEventRecord(side->join, ss));
     ysh = l.ysh;
   }
+  if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,
+                       tiles_done)) != MOE_OK)
+    return s;
+  if (shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
   MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, y, c.tokens, c.hidden, c.top_k, st));
   return MOE_OK;
 }

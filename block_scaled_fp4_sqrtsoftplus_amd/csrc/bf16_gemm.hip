@@ -282,6 +282,76 @@ static hipError_t launch_skinny(const uint16_t* X, const uint16_t* W, const uint
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Router logits of a small batch (M <= 64 tokens): the gate matrix is only
+// E x H bf16 (2 MB at E = 256), so the whole read must be in flight at once.
+// Workgroup (nb, ks) of 8 waves owns 16 experts and the K slice
+// [ks K/KS, (ks+1) K/KS); each wave loads its 1/8 of that slice in one go
+// (no loop), the 8 partial sums meet in a fixed-order LDS tree, and the
+// workgroup writes partial[ks][t][e].  The top-k kernel adds the KS partials
+// in ks order, so the logits do not depend on timing.
+// ---------------------------------------------------------------------------
+template <int MT, int STEPS>
+__global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __restrict__ X,
+                                                            const uint16_t* __restrict__ W,
+                                                            float* __restrict__ partial, int M,
+                                                            int N, int K, int KS) {
+  constexpr int NACC = MT * 4;
+  __shared__ float red[4][NACC][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int ks = blockIdx.y;
+  const int k0 = ks * (K / KS) + wv * STEPS * 32;
+  const uint16_t* wp = W + (size_t)min(n0 + col, N - 1) * K + k0 + 8 * grp;
+  uint4 A[STEPS], B[STEPS][MT];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    A[s] = *reinterpret_cast<const uint4*>(wp + s * 32);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      B[s][m] = *reinterpret_cast<const uint4*>(X + (size_t)min(16 * m + col, M - 1) * K + k0 +
+                                                8 * grp + s * 32);
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(A[s], B[s][m], acc[m]);
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (wv >= half && wv < 2 * half) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wv - half][4 * m + v][lane] = acc[m][v];
+    }
+    __syncthreads();
+    if (wv < half) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[m][v] += red[wv][4 * m + v][lane];
+    }
+    __syncthreads();
+  }
+  if (wv != 0) return;
+  float* out = partial + (size_t)ks * M * N;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int r = 16 * m + col;
+    if (r >= M) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = n0 + 4 * grp + v;
+      if (c < N) out[(size_t)r * N + c] = acc[m][v];
+    }
+  }
+}
+
 template <int EPI, int TPW>
 static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* W3, void* out,
                               int64_t M, int N, int K, float limit, hipStream_t st) {
@@ -302,6 +372,37 @@ static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
                               int H, int E, hipStream_t st) {
   return launch_bf16<EPI_F32, 1>(x, wg, nullptr, logits, T, E, H, 0.f, st);
+}
+
+int router_splits(int64_t T, int H) {
+  // per-wave K steps of 32: 1, 2 or 4 are instantiated
+  const int unit = kRouterSplits * 8 * 32;
+  const int steps = H / unit;
+  const bool ok = H % unit == 0 && (steps == 1 || steps == 2 || steps == 4);
+  return (T >= 1 && T <= 64 && ok) ? kRouterSplits : 1;
+}
+
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
+                                 int H, int E, hipStream_t st) {
+  const int KS = kRouterSplits;
+  const int steps = H / KS / 8 / 32;   // per wave
+  const dim3 grid((unsigned)((E + 15) / 16), (unsigned)KS);
+  const int M = (int)T;
+#define MOE_ROUTER_LAUNCH(MT, ST) \
+  hipLaunchKernelGGL((router_splitk_kernel<MT, ST>), grid, dim3(512), 0, st, x, wg, partial, M, E, H, KS)
+  const int mt = (M + 15) / 16;
+  if (steps == 2) {
+    if (mt == 1) MOE_ROUTER_LAUNCH(1, 2); else if (mt == 2) MOE_ROUTER_LAUNCH(2, 2);
+    else if (mt == 3) MOE_ROUTER_LAUNCH(3, 2); else MOE_ROUTER_LAUNCH(4, 2);
+  } else if (steps == 4) {
+    if (mt == 1) MOE_ROUTER_LAUNCH(1, 4); else if (mt == 2) MOE_ROUTER_LAUNCH(2, 4);
+    else if (mt == 3) MOE_ROUTER_LAUNCH(3, 4); else MOE_ROUTER_LAUNCH(4, 4);
+  } else {  // steps == 1 (router_splits admits only 1, 2, 4)
+    if (mt == 1) MOE_ROUTER_LAUNCH(1, 1); else if (mt == 2) MOE_ROUTER_LAUNCH(2, 1);
+    else if (mt == 3) MOE_ROUTER_LAUNCH(3, 1); else MOE_ROUTER_LAUNCH(4, 1);
+  }
+#undef MOE_ROUTER_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,

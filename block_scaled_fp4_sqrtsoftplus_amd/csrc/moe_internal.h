@@ -69,8 +69,19 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
                               int H, int E, hipStream_t st);
 
-hipError_t launch_score_topk(const float* logits, const float* bias, int64_t T, int E, int k,
-                             float route_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);
+// Router logits of a small batch as kRouterSplits partial sums over K:
+// partial[ks][t][e]; router_splits() says whether this path applies (T <= 64
+// and H a multiple of kRouterSplits * 512), else it returns 1.
+constexpr int kRouterSplits = 8;
+int router_splits(int64_t T, int H);
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
+                                 int H, int E, hipStream_t st);
+
+// Scores + top-k from logits given as `splits` partial sums [splits][T][E]
+// (added in split order); logits_out (or NULL) receives their sum.
+hipError_t launch_score_topk(const float* logits, int splits, float* logits_out, const float* bias,
+                             int64_t T, int E, int k, float route_scale, int32_t* topk_idx,
+                             float* topk_w, hipStream_t st);
 
 hipError_t launch_hash_route(const int64_t* token_ids, int64_t T, int E, int k,
                              float route_scale, uint64_t seed, int32_t* topk_idx, float* topk_w,
@@ -81,6 +92,13 @@ size_t permute_scratch_bytes(int64_t P, int E);
 hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* expert_offsets,
                           int32_t* sorted_pairs, int32_t* pair_pos, void* scratch,
                           hipStream_t st);
+
+// Permutation + m-tile prefix (tiles of bm pairs) of a small batch
+// (P <= kFusedMaxPairs, E <= 512) in one workgroup.
+constexpr int kFusedMaxPairs = 2048;
+hipError_t launch_perm_fused(const int32_t* topk_idx, int P, int E, int bm, int32_t* offsets,
+                             int32_t* sorted_pairs, int32_t* pair_pos, int32_t* mtile_off,
+                             hipStream_t st);
 
 // Tile prefix of the grouped GEMMs: mtile_off[e] = sum_{e'<e} ceil(n_e'/bm).
 hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int32_t* mtile_off,

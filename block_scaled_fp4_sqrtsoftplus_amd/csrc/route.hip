@@ -5,8 +5,9 @@
 //  score_topk  one wave per token; lane l owns experts l, l+64, ...; the score
 //              s = sqrt(ln(1 + e^z)) is evaluated in double and rounded to fp32;
 //              key = s + bias; k rounds of a wave arg-max (larger key first,
-//              lower expert id on equal keys); weights s_j / sum(s) * scale in
-//              fp32 with the sum taken in rank order (IEEE division).
+//              lower expert id on equal keys) built from two DPP wave
+//              reductions each; weights s_j / sum(s) * scale in fp32 with the
+//              sum taken in rank order (IEEE division).
 //  hash_route  one thread per token: SplitMix64 (Steele, Lea, Flood, OOPSLA
 //              2014) from (seed << 32) ^ token_id; r mod E with r at or above
 //              2^64 - (2^64 mod E) rejected, repeats skipped, first k kept.
@@ -21,7 +22,20 @@ namespace moe {
 
 constexpr int kMaxExpertsPerLane = 8;  // E <= 512
 
+extern "C" __device__ unsigned int __ockl_wfred_max_u32(unsigned int);
+extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
+
+// Order-preserving map of a finite fp32 key to uint32 (larger key -> larger
+// integer; equal keys -> equal integers, as +0 and -0 cannot both occur:
+// keys are s + b with s > 0).  Every finite key maps above 0x007FFFFF, so 0
+// marks a retired or absent expert.
+__device__ __forceinline__ uint32_t key_order(float k) {
+  const uint32_t u = __float_as_uint(k);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict__ logits,
+                                                         int splits, float* __restrict__ logits_out,
                                                          const float* __restrict__ bias,
                                                          int64_t T, int E, int k,
                                                          float route_scale,
@@ -31,46 +45,60 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* z = logits + t * E;
-  float s[kMaxExpertsPerLane], key[kMaxExpertsPerLane];
+  const size_t split_stride = (size_t)T * E;
+  float s[kMaxExpertsPerLane];
+  uint32_t ok[kMaxExpertsPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
     const int ex = lane + 64 * i;
     if (ex < E) {
-      const double zd = (double)z[ex];
+      float zf;
+      if (splits == kRouterSplits) {
+        // all partial loads in flight first, then the fixed-order sum
+        float part[kRouterSplits];
+#pragma unroll
+        for (int p = 0; p < kRouterSplits; ++p) part[p] = z[p * split_stride + ex];
+        zf = part[0];
+#pragma unroll
+        for (int p = 1; p < kRouterSplits; ++p) zf += part[p];
+      } else {
+        zf = z[ex];
+        for (int p = 1; p < splits; ++p) zf += z[p * split_stride + ex];
+      }
+      if (logits_out) logits_out[t * E + ex] = zf;
+      const double zd = (double)zf;
       s[i] = (float)sqrt(log1p(exp(zd)));
-      key[i] = bias ? s[i] + bias[ex] : s[i];
+      ok[i] = key_order(bias ? s[i] + bias[ex] : s[i]);
     } else {
       s[i] = 0.f;
-      key[i] = -INFINITY;
+      ok[i] = 0u;
     }
   }
   int sel_e[8];
   float sel_s[8];
   for (int j = 0; j < k; ++j) {
-    // lane-local best (ascending expert order makes '>' keep the lower id)
-    float bk = -INFINITY;
-    int be = 0x7FFFFFFF;
+    // lane-local best: largest key, lower expert id on equal keys (slots are
+    // visited in ascending expert order, so '>' keeps the lower id)
+    uint32_t bk = 0u;
+    uint32_t be = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-      const int ex = lane + 64 * i;
-      if (ex < E && (key[i] > bk || (key[i] == bk && ex < be))) { bk = key[i]; be = ex; }
-    }
-    // wave arg-max: (key desc, expert asc) is a total order, so the butterfly
-    // gives every lane the same winner
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oe = __shfl_xor(be, off);
-      if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; }
-    }
-    sel_e[j] = be;
-    // owner lane retires the winner and publishes its unbiased score
+    for (int i = 0; i < kMaxExpertsPerLane; ++i)
+      if (ok[i] > bk) { bk = ok[i]; be = (uint32_t)(lane + 64 * i); }
+    // wave arg-max in two DPP reductions: the largest key, then the lowest
+    // expert id among the lanes holding it
+    const uint32_t m = __ockl_wfred_max_u32(bk);
+    const int win = (int)__ockl_wfred_min_u32(bk == m ? be : 0xFFFFFFFFu);
+    sel_e[j] = win;
+    // the owner lane retires the winner; its unbiased score is broadcast
+    const int wl = win & 63, wi = win >> 6;
     float ws = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-      if (lane + 64 * i == be) { ws = s[i]; key[i] = -INFINITY; }
-    }
-    sel_s[j] = __shfl(ws, be & 63);
+    for (int i = 0; i < kMaxExpertsPerLane; ++i)
+      if (i == wi) {
+        ws = s[i];
+        if (lane == wl) ok[i] = 0u;
+      }
+    sel_s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
   }
   if (lane == 0) {
     float total = 0.f;
@@ -82,12 +110,12 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
   }
 }
 
-hipError_t launch_score_topk(const float* logits, const float* bias, int64_t T, int E, int k,
-                             float route_scale, int32_t* topk_idx, float* topk_w,
-                             hipStream_t st) {
+hipError_t launch_score_topk(const float* logits, int splits, float* logits_out, const float* bias,
+                             int64_t T, int E, int k, float route_scale, int32_t* topk_idx,
+                             float* topk_w, hipStream_t st) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits,
-                     bias, T, E, k, route_scale, topk_idx, topk_w);
+                     splits, logits_out, bias, T, E, k, route_scale, topk_idx, topk_w);
   return hipGetLastError();
 }
 
@@ -140,6 +168,21 @@ hipError_t launch_hash_route(const int64_t* ids, int64_t T, int E, int k, float 
 // ---------------------------------------------------------------------------
 // Permutation
 // ---------------------------------------------------------------------------
+// Mask of the lanes holding the same value as this lane: one ballot per
+// distinct value present in the wave (the lowest unresolved lane's value is
+// read as a scalar and compared by every lane), instead of 64 shuffles.
+__device__ __forceinline__ uint64_t lanes_with_same(int v) {
+  uint64_t same = 0;
+  uint64_t todo = __ballot(1);
+  while (todo) {
+    const int leader = __builtin_ctzll(todo);
+    const int lv = __builtin_amdgcn_readlane(v, leader);
+    const uint64_t m = __ballot(v == lv);
+    if (v == lv) same = m;
+    todo &= ~m;
+  }
+  return same;
+}
 constexpr int kPermChunk = 1024;  // pairs per chunk (one wave walks 16 rounds of 64)
 
 size_t permute_scratch_bytes(int64_t P, int E) {
@@ -210,12 +253,8 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t* __restr
     const int64_t p = r0 + lane;
     const bool live = p < hi;
     const int ex = live ? idx[p] : -1;
-    // lanes with the same expert: compare against every lane's value
-    uint64_t same = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int oj = __shfl(ex, j);
-      same |= (uint64_t)(oj == ex) << j;
-    }
+    // lanes with the same expert
+    const uint64_t same = lanes_with_same(ex);
     const uint64_t lower = same & ((1ull << lane) - 1ull);
     const int rank = __popcll(lower);
     const int cnt = __popcll(same);
@@ -276,6 +315,104 @@ hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int3
                               hipStream_t st) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(512), 0, st, expert_offsets, E, bm,
                      mtile_off);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Small batches (P = T*k <= kFusedMaxPairs): the permutation and the grouped
+// GEMMs' m-tile prefix in one workgroup of 16 waves -- expert histogram,
+// exclusive scan, stable scatter, m-tile prefix -- one launch instead of
+// four.  Same result as the multi-kernel path: counts come from LDS
+// histograms, and the scatter keeps pair order within each expert (wave w
+// owns the w-th contiguous chunk of pairs; its base per expert is the sum of
+// the lower chunks' counts).
+// ---------------------------------------------------------------------------
+constexpr int kFusedWaves = 16;
+
+__global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
+    const int32_t* __restrict__ topk_idx, int P, int E, int bm, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ mtile_off) {
+  __shared__ int32_t sel[kFusedMaxPairs];
+  __shared__ int32_t wcnt[kFusedWaves][512];   // per-wave counts, then per-wave bases
+  __shared__ int32_t tot[512];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  for (int p = threadIdx.x; p < P; p += kFusedWaves * 64) sel[p] = topk_idx[p];
+  for (int i = threadIdx.x; i < kFusedWaves * 512; i += kFusedWaves * 64) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+
+  // per-wave histograms over contiguous pair chunks
+  const int chunk = (P + kFusedWaves - 1) / kFusedWaves;
+  const int p_lo = min(P, wv * chunk), p_hi = min(P, p_lo + chunk);
+  for (int p = p_lo + lane; p < p_hi; p += 64) atomicAdd(&wcnt[wv][sel[p]], 1);
+  __syncthreads();
+
+  // expert totals, exclusive scan, per-wave bases
+  const int e = threadIdx.x;  // E <= 512 < 1024 threads
+  int32_t sum = 0;
+  if (e < E)
+    for (int w = 0; w < kFusedWaves; ++w) sum += wcnt[w][e];
+  if (e < 512) tot[e] = sum;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    int32_t v = 0;
+    if (e < 512 && e >= off) v = tot[e - off];
+    __syncthreads();
+    if (e < 512) tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    int32_t base = tot[e] - sum;
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = tot[e];
+    for (int w = 0; w < kFusedWaves; ++w) {
+      const int32_t n = wcnt[w][e];
+      wcnt[w][e] = base;
+      base += n;
+    }
+  }
+  __syncthreads();
+  // m-tile prefix (reuses tot[]): ceil(count / bm) per expert
+  const int32_t c = (e < E) ? (sum + bm - 1) / bm : 0;
+  if (e < 512) tot[e] = c;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    int32_t v = 0;
+    if (e < 512 && e >= off) v = tot[e - off];
+    __syncthreads();
+    if (e < 512) tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    mtile_off[e] = tot[e] - c;
+    if (e == E - 1) mtile_off[E] = tot[e];
+  }
+
+  // stable scatter, each wave over its chunk in order
+  for (int r0 = p_lo; r0 < p_hi; r0 += 64) {
+    const int p = r0 + lane;
+    const bool live = p < p_hi;
+    const int ex = live ? sel[p] : -1;
+    const uint64_t same = lanes_with_same(ex);
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (live) {
+      const int pos = wcnt[wv][ex] + rank;
+      sorted_pairs[pos] = p;
+      pair_pos[p] = pos;
+    }
+    // wave-synchronous: every lane has read its base before the highest
+    // lane of each expert advances it
+    if (live && (same >> lane) == 1ull) wcnt[wv][ex] += __popcll(same);
+  }
+}
+
+hipError_t launch_perm_fused(const int32_t* topk_idx, int P, int E, int bm, int32_t* offsets,
+                             int32_t* sorted_pairs, int32_t* pair_pos, int32_t* mtile_off,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(perm_fused_kernel, dim3(1), dim3(kFusedWaves * 64), 0, st, topk_idx, P, E,
+                     bm, offsets, sorted_pairs, pair_pos, mtile_off);
   return hipGetLastError();
 }
 

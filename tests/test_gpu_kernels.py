@@ -275,7 +275,8 @@ def test_expert_ffn_unclamped_limit():
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
 
 
-@pytest.mark.parametrize("T,E,H", [(1, 40, 1024), (17, 256, 4096), (37, 33, 2048), (64, 384, 4096)])
+@pytest.mark.parametrize("T,E,H", [(1, 40, 1024), (17, 256, 4096), (37, 33, 2048), (64, 384, 4096),
+                                   (5, 64, 8192), (64, 256, 6144)])
 def test_router_logits_small_batches(T, E, H):
     # the decode-sized router GEMM (K split over 8 waves, LDS tree reduction)
     wl = synth.WORKLOADS["decode"].replace(n_experts=E, hidden=H)
