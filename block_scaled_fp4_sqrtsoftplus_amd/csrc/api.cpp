@@ -184,10 +184,14 @@ moe_status check_weights(const moe_expert_weights* w) {
   return MOE_OK;
 }
 
-// Tokens per m-tile of the grouped GEMMs, from the mean pairs per expert.
+// Tokens per m-tile of the grouped GEMMs, from the mean pairs per expert:
+// 16 (decode-like), 128 (prefill-like, when both K are 1024, 2048 or 4096),
+// else 64.
 int choose_bm(const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
-  return P <= (int64_t)32 * c.n_experts ? 16 : 64;
+  if (P <= (int64_t)32 * c.n_experts) return 16;
+  auto tiled = [](int k) { return k == 1024 || k == 2048 || k == 4096; };
+  return (tiled(c.hidden) && tiled(c.inter)) ? 128 : 64;
 }
 
 // Routing (S1-S3).  Small batches run the single-workgroup permutation

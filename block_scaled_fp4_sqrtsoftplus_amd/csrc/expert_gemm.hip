@@ -511,6 +511,264 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tile variant for m-tiles of 128 pairs (prefill) when K is 1024, 2048 or
+// 4096.  Each of the four waves owns 4 weight tiles (64 rows) streamed into
+// registers through a two-step ring (each weight row's scale line read once,
+// as in the streaming kernel); the 128 activation rows of a K step are staged
+// through double-buffered LDS and read by all four waves; the 128 tokens'
+// per-128 activation scales sit in LDS for the whole tile.  Per K step a wave
+// issues 32 MFMAs: for each 16-token sub-tile, one group of 4 (one per weight
+// tile) from a single asm block whose trailing wait states protect all four
+// instructions' operands.  Accumulators live in AGPRs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mfma4_fp4_fp8(v4f& c0, v4f& c1, v4f& c2, v4f& c3,
+                                              const uint4 (&a)[4], const uint4& b0,
+                                              const uint4& b1, int s0, int s1, int s2, int s3,
+                                              int sb) {
+  const v4i a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w};
+  const v4i a1 = {(int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+  const v4i a2 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w};
+  const v4i a3 = {(int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
+  const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                  (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  asm volatile(
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %4, %8, %0, %9, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %5, %8, %1, %10, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %6, %8, %2, %11, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %7, %8, %3, %12, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(bv), "v"(s0), "v"(s1), "v"(s2), "v"(s3),
+        "v"(sb));
+}
+
+template <int MODE, int S>
+__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmArgs p, int mt_max,
+                                                                     int n_tiles) {
+  constexpr int MT = 8, BM = 128;
+  constexpr int K = S * 128;
+  constexpr int SD = S / 4;
+  constexpr int LDS_ROW = 144;
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[2][BM][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t bsc[BM][S];
+  __shared__ float red[4][BM];
+
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile(p, mt_max, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int N = p.N;
+  const size_t wrow_bytes = (size_t)K / 2;
+  const size_t srow_bytes = (size_t)K / 32;
+
+  const uint8_t* wptr[4];
+  const uint8_t* sptr[4];
+  int n0;
+  bool wave_live = true;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const uint8_t* base = (t < 2) ? p.w : p.w3;
+      const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
+      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes;
+    }
+  } else {
+    n0 = n_tile * kG2Rows;
+    wave_live = (n0 + 64 * wv) < N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
+      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+    }
+  }
+  // staging: thread tid copies half (64 bytes) of token row tid/2's K step;
+  // slots past the expert's last pair read that last pair's row (dropped)
+  const int st_tok = tid >> 1, st_half = tid & 1;
+  int64_t st_row;
+  {
+    const int slot = min(m0 + st_tok, n_e - 1);
+    st_row = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
+                         : (int64_t)(off_e + slot);
+  }
+  const uint8_t* st_src = p.a + st_row * K + 64 * st_half;
+
+  // token scales of the whole tile into LDS
+  {
+    const uint8_t* src = p.a_scale + st_row * S + st_half * (S / 2);
+    uint8_t* dst = &bsc[st_tok][st_half * (S / 2)];
+    if constexpr (S == 32) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    } else if constexpr (S == 16) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    }
+  }
+
+  // weight scale lines (a quarter per lane group)
+  uint32_t SR[4][SD];
+  if (wave_live) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* src = sptr[t] + grp * S;
+      if constexpr (SD >= 4) {
+#pragma unroll
+        for (int j = 0; j < SD / 4; ++j) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * j);
+          SR[t][4 * j] = v.x; SR[t][4 * j + 1] = v.y; SR[t][4 * j + 2] = v.z; SR[t][4 * j + 3] = v.w;
+        }
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        SR[t][0] = v.x; SR[t][1] = v.y;
+      }
+    }
+  }
+
+  v4f acc[4][MT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 A0[4], A1[4];
+  v4i ST[4];
+  auto load_a = [&](int s, uint4 (&a)[4]) {
+    if (wave_live) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
+    }
+  };
+  // native vector type: a loop of struct copies would become a memcpy
+  // through private memory
+  auto load_st = [&](int s, v4i (&v)[4]) {
+    const v4i* src = reinterpret_cast<const v4i*>(st_src + (size_t)s * 128);
+    v[0] = src[0]; v[1] = src[1]; v[2] = src[2]; v[3] = src[3];
+  };
+  auto store_st = [&](uint8_t* dst, const v4i (&v)[4]) {
+    v4i* d = reinterpret_cast<v4i*>(dst);
+    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+  };
+  uint8_t* const st_dst0 = &bsm[0][st_tok][64 * st_half];
+  uint8_t* const st_dst1 = &bsm[1][st_tok][64 * st_half];
+  // one K step from LDS buffer `buf` and weight ring slot `a`
+  auto compute = [&](int s, int buf, const uint4 (&a)[4]) {
+    if (!wave_live) return;
+    const int src_lane = col + 16 * (s / SD);
+    int sa[4];
+    // dw = s % SD: SD is a power of two
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t w = SR[t][0];
+#pragma unroll
+      for (int j = 1; j < SD; ++j) w = ((s & (SD - 1)) == j) ? SR[t][j] : w;
+      sa[t] = __shfl((int)w, src_lane) >> (8 * grp);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint4 b0 = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][16 * grp]);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][64 + 16 * grp]);
+      const int sb = bsc[16 * m + col][s];
+      mfma4_fp4_fp8(acc[0][m], acc[1][m], acc[2][m], acc[3][m], a, b0, b1, sa[0], sa[1], sa[2],
+                    sa[3], sb);
+    }
+  };
+
+  // S is even.  Loads past the last step re-read step S-1 (cache hits) so
+  // that the loop body has no conditional loads; each LDS buffer is written
+  // only after the barrier that follows the last read of it.
+  static_assert(S % 2 == 0, "even number of K steps");
+  load_a(0, A0);
+  load_a(1, A1);
+  load_st(0, ST);
+  store_st(st_dst0, ST);
+  __syncthreads();
+  load_st(1, ST);
+  for (int s = 0; s < S; s += 2) {
+    compute(s, 0, A0);                 // even step: ring slot A0, LDS buffer 0
+    load_a(min(s + 2, S - 1), A0);
+    store_st(st_dst1, ST);
+    __syncthreads();
+    load_st(min(s + 2, S - 1), ST);
+    compute(s + 1, 1, A1);             // odd step: ring slot A1, LDS buffer 1
+    load_a(min(s + 3, S - 1), A1);
+    store_st(st_dst0, ST);
+    __syncthreads();
+    load_st(min(s + 3, S - 1), ST);
+  }
+
+  if (MODE == 1) {
+    // clamped SwiGLU, per-128 FP8 requant of h over this tile's 128 columns
+    const float lim = p.limit;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float amax = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g = fminf(fmaxf(acc[tt][m][v], -lim), lim);
+          const float u = fminf(fmaxf(acc[tt + 2][m][v], -lim), lim);
+          const float hv = silu_f(g) * u;
+          acc[tt][m][v] = hv;                       // h kept in the w1 slots
+          amax = fmaxf(amax, fabsf(hv));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if (lane < 16) red[wv][16 * m + lane] = amax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int tokc = 16 * m + col;
+      const float amax = fmaxf(fmaxf(red[0][tokc], red[1][tokc]), fmaxf(red[2][tokc], red[3][tokc]));
+      const int ex = pow2_scale_exp(amax);
+      const int slot = m0 + tokc;
+      if (slot < n_e) {
+        const size_t row = (size_t)(off_e + slot);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(acc[tt][m][v], -ex)) << (8 * v);
+          *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
+        }
+        if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+      }
+    }
+  } else {
+    if (!wave_live) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int slot = m0 + 16 * m + col;
+      if (slot >= n_e) continue;
+      const size_t row = (size_t)(off_e + slot);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
+        if (p.out_fp32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
+              make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+        } else {
+          const uint32_t lo = f32_to_bf16(acc[t][m][0]) | (f32_to_bf16(acc[t][m][1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[t][m][2]) | (f32_to_bf16(acc[t][m][3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
+              make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
 static inline unsigned pad8(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
 
 template <int MODE>
@@ -518,7 +776,18 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (bm == 16 && a.K == 4096) {
+  if (bm == 128) {
+    if (a.K != 1024 && a.K != 2048 && a.K != 4096) return hipErrorInvalidValue;
+    if (a.K == 4096)
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+    else if (a.K == 2048)
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 16>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+    else
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 8>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+  } else if (bm == 16 && a.K == 4096) {
     hipLaunchKernelGGL((expert_gemm_stream<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   } else if (bm == 16 && a.K == 2048) {

@@ -231,6 +231,10 @@ def _check_o(o, hq, hs, ref, r, absw2):
     ("decode", 10, dict(hidden=1024, inter=1024, n_experts=8)),             # K = 1024 streaming path
     ("decode", 6, dict(hidden=2048, inter=4096, n_experts=6, top_k=2)),     # K = 2048 / 4096 swapped
     ("tiny", 19, dict(hidden=768, inter=640, n_experts=5, top_k=5, exp_lo=-9, exp_hi=-7)),
+    # > 32 pairs per expert with K in {1024, 2048, 4096}: 128-token tiles
+    ("decode", 600, dict(hidden=1024, inter=1024, n_experts=8, top_k=2)),
+    ("decode", 300, dict(hidden=2048, inter=4096, n_experts=4, top_k=2)),
+    ("decode", 400, dict(n_experts=8, top_k=2)),
 ])
 def test_expert_ffn_parity(shape):
     name, tokens, over = shape

@@ -49,6 +49,7 @@ def check_routing_valid(r, T, k, E):
     ("tiny", 33, dict(mode="hash", n_experts=20, top_k=6, hidden=384, inter=256, shared=True)),
     ("tiny", 1, dict(n_experts=8, top_k=8)),
     ("decode", 5, dict(n_experts=12)),
+    ("decode", 300, dict(hidden=1024, inter=1024, n_experts=4, top_k=2, shared=True)),
 ])
 def test_layer_parity_small(shape):
     name, tokens, over = shape
