@@ -98,6 +98,36 @@ __device__ __forceinline__ bool map_tile(const ExpertGemmArgs& p, int mt_max, in
   return true;
 }
 
+// Expert-major tile order for large m-tiles: the tiles of one expert are
+// consecutive, m-tile fastest (an n-slice of its weights is used by all of
+// its m-tiles back to back, and its activation rows by all n-slices close in
+// time), and each XCD (workgroups are dispatched to the 8 XCDs round-robin)
+// takes one contiguous eighth of the real tiles, so that the workgroups
+// sharing an L2 share weights and activations.
+__device__ __forceinline__ bool map_tile_grouped(const ExpertGemmArgs& p, int n_tiles, int bm,
+                                                 int& n_tile, int& e, int& m0, int& off_e,
+                                                 int& n_e) {
+  const int b = blockIdx.x;
+  const int total = p.mtile_off[p.E] * n_tiles;
+  const int share = (total + 7) >> 3;
+  const int r = b >> 3;
+  const int u = (b & 7) * share + r;
+  if (r >= share || u >= total) return false;
+  int lo = 0, hi = p.E;  // mtile_off[lo] * n_tiles <= u < mtile_off[hi] * n_tiles
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.mtile_off[mid] * n_tiles <= u) lo = mid; else hi = mid;
+  }
+  e = lo;
+  const int m_e = p.mtile_off[e + 1] - p.mtile_off[e];
+  const int local = u - p.mtile_off[e] * n_tiles;
+  n_tile = local / m_e;
+  m0 = (local - n_tile * m_e) * bm;
+  off_e = p.expert_offsets[e];
+  n_e = p.expert_offsets[e + 1] - off_e;
+  return true;
+}
+
 template <int MODE, int MT>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {
@@ -514,34 +544,48 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
 // ---------------------------------------------------------------------------
 // Tile variant for m-tiles of 128 pairs (prefill) when K is 1024, 2048 or
 // 4096.  Each of the four waves owns 4 weight tiles (64 rows) streamed into
-// registers through a two-step ring (each weight row's scale line read once,
-// as in the streaming kernel); the 128 activation rows of a K step are staged
-// through double-buffered LDS and read by all four waves; the 128 tokens'
-// per-128 activation scales sit in LDS for the whole tile.  Per K step a wave
-// issues 32 MFMAs: for each 16-token sub-tile, one group of 4 (one per weight
-// tile) from a single asm block whose trailing wait states protect all four
-// instructions' operands.  Accumulators live in AGPRs.
+// registers through a four-step ring (each weight row's scale line read
+// once, as in the streaming kernel).  The 128 activation rows of a K step are
+// loaded two steps ahead into registers, written to one of four LDS buffers
+// at the end of the step before their use, and read by all four waves; the
+// 128 tokens' per-128 activation scales sit in LDS for the whole tile.  Per
+// K step a wave issues 32 MFMAs in four asm blocks of 8 (two 16-token
+// sub-tiles x four weight tiles), each closed by the wait states that
+// protect its operands.  Accumulators live in AGPRs.
+//
+// LDS activation layout: token t's 16-byte chunk c (bytes 16c..16c+15 of the
+// step) sits at slot c ^ (t & 7) ^ ((t >> 3) & 1) of the token's 128-byte
+// line, so that the 16-byte reads of 16 consecutive tokens (same c) hit
+// distinct banks.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void mfma4_fp4_fp8(v4f& c0, v4f& c1, v4f& c2, v4f& c3,
-                                              const uint4 (&a)[4], const uint4& b0,
-                                              const uint4& b1, int s0, int s1, int s2, int s3,
-                                              int sb) {
-  const v4i a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w};
-  const v4i a1 = {(int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
-  const v4i a2 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w};
-  const v4i a3 = {(int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
-  const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                  (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-  asm volatile(
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %4, %8, %0, %9, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %5, %8, %1, %10, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %6, %8, %2, %11, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %7, %8, %3, %12, %13 op_sel_hi:[0,0,0] cbsz:4\n\t"
+__device__ __forceinline__ int tile_slot(int t, int c) { return c ^ (t & 7) ^ ((t >> 3) & 1); }
+
+// Two 16-token sub-tiles (B operands b0/b1, scales sb0/sb1) against four
+// weight tiles (a[0..3], scales sa0..sa3).
+__device__ __forceinline__ void mfma8_fp4_fp8(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+                                              const v8i& b0, const v8i& b1, int sa0, int sa1,
+                                              int sa2, int sa3, int sb0, int sb1) {
+  asm(
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %12, %0, %14, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %9, %12, %1, %15, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %10, %12, %2, %16, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %11, %12, %3, %17, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %8, %13, %4, %14, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %9, %13, %5, %15, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %10, %13, %6, %16, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %11, %13, %7, %17, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
       "s_nop 15\n\t"
       "s_nop 15"
-      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(bv), "v"(s0), "v"(s1), "v"(s2), "v"(s3),
-        "v"(sb));
+      : "+a"(c0[0]), "+a"(c0[1]), "+a"(c0[2]), "+a"(c0[3]),
+        "+a"(c1[0]), "+a"(c1[1]), "+a"(c1[2]), "+a"(c1[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b0), "v"(b1),
+        "v"(sa0), "v"(sa1), "v"(sa2), "v"(sa3), "v"(sb0), "v"(sb1));
+}
+
+// Workgroup barrier once this wave's LDS writes are done; no memory access
+// is moved across it (outstanding global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int MODE, int S>
@@ -550,13 +594,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   constexpr int MT = 8, BM = 128;
   constexpr int K = S * 128;
   constexpr int SD = S / 4;
-  constexpr int LDS_ROW = 144;
-  __shared__ __attribute__((aligned(16))) uint8_t bsm[2][BM][LDS_ROW];
+  static_assert(S % 4 == 0 && S >= 8, "K steps in groups of four, at least two groups");
+  // four activation buffers (one per step of a group of four)
+  __shared__ __attribute__((aligned(1024))) uint8_t act0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t act1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t act2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t act3[BM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t bsc[BM][S];
   __shared__ float red[4][BM];
+  (void)mt_max;
 
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile(p, mt_max, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_tile_grouped(p, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -591,20 +640,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
       sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
     }
   }
-  // staging: thread tid copies half (64 bytes) of token row tid/2's K step;
-  // slots past the expert's last pair read that last pair's row (dropped)
-  const int st_tok = tid >> 1, st_half = tid & 1;
-  int64_t st_row;
-  {
-    const int slot = min(m0 + st_tok, n_e - 1);
-    st_row = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
-                         : (int64_t)(off_e + slot);
-  }
-  const uint8_t* st_src = p.a + st_row * K + 64 * st_half;
 
-  // token scales of the whole tile into LDS
+  // activation source row of tile token t (slots past the expert's last pair
+  // read that last pair's row; their results are dropped)
+  auto src_row = [&](int t) -> int64_t {
+    const int slot = min(m0 + t, n_e - 1);
+    return (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
+                       : (int64_t)(off_e + slot);
+  };
+
+  // Activation staging: this thread moves 4 x 16 bytes per step, for tokens
+  // 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the token's
+  // line, i.e. chunk slot ^ (t & 7) ^ ((t >> 3) & 1) of the step (the map is
+  // an involution on the chunk index)
+  const uint8_t* ssrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 32 * wv + 8 * j + (lane >> 3);
+    ssrc[j] = p.a + src_row(t) * K + 16 * tile_slot(t, lane & 7);
+  }
+  const int sdst = (32 * wv + (lane >> 3)) * 128 + 16 * (lane & 7);  // + 1024 * j
+  v4i R[2][4];
+  auto stage_load = [&](int s, v4i (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const v4i*>(ssrc[j] + (size_t)s * 128);
+  };
+  auto stage_store = [&](uint8_t* buf, const v4i (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(buf + sdst + 1024 * j) = r[j];
+  };
+
+  // token scales of the whole tile into LDS: thread tid copies half of
+  // token tid/2's scale line
   {
-    const uint8_t* src = p.a_scale + st_row * S + st_half * (S / 2);
+    const int st_tok = tid >> 1, st_half = tid & 1;
+    const uint8_t* src = p.a_scale + src_row(st_tok) * S + st_half * (S / 2);
     uint8_t* dst = &bsc[st_tok][st_half * (S / 2)];
     if constexpr (S == 32) {
       *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
@@ -617,7 +687,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 
   // weight scale lines (a quarter per lane group)
   uint32_t SR[4][SD];
-  if (wave_live) {
+  {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint8_t* src = sptr[t] + grp * S;
@@ -634,38 +704,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     }
   }
 
-  v4f acc[4][MT];
+  v4f acc[MT][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[m][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 A0[4], A1[4];
-  v4i ST[4];
-  auto load_a = [&](int s, uint4 (&a)[4]) {
-    if (wave_live) {
+  v4i A[4][4];  // weight ring: [step % 4][tile]
+  // (waves without weight rows load row 0 too: unconditional loads keep the
+  // compiler's load counting exact)
+  auto load_a = [&](int s, v4i (&a)[4]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-    }
+    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4i*>(wptr[t] + (size_t)s * 64);
   };
-  // native vector type: a loop of struct copies would become a memcpy
-  // through private memory
-  auto load_st = [&](int s, v4i (&v)[4]) {
-    const v4i* src = reinterpret_cast<const v4i*>(st_src + (size_t)s * 128);
-    v[0] = src[0]; v[1] = src[1]; v[2] = src[2]; v[3] = src[3];
-  };
-  auto store_st = [&](uint8_t* dst, const v4i (&v)[4]) {
-    v4i* d = reinterpret_cast<v4i*>(dst);
-    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-  };
-  uint8_t* const st_dst0 = &bsm[0][st_tok][64 * st_half];
-  uint8_t* const st_dst1 = &bsm[1][st_tok][64 * st_half];
-  // one K step from LDS buffer `buf` and weight ring slot `a`
-  auto compute = [&](int s, int buf, const uint4 (&a)[4]) {
+
+  // one K step: activations from `buf`, weights from ring slot `a`; the
+  // four steps of a group share one dword of token scales per sub-tile
+  uint32_t sbw[MT];
+  auto compute = [&](int s, const uint8_t* buf, const v4i (&a)[4]) {
     if (!wave_live) return;
+    if ((s & 3) == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        sbw[m] = *reinterpret_cast<const uint32_t*>(&bsc[16 * m + col][s]);
+    }
     const int src_lane = col + 16 * (s / SD);
     int sa[4];
-    // dw = s % SD: SD is a power of two
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t w = SR[t][0];
@@ -673,38 +737,53 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
       for (int j = 1; j < SD; ++j) w = ((s & (SD - 1)) == j) ? SR[t][j] : w;
       sa[t] = __shfl((int)w, src_lane) >> (8 * grp);
     }
+    const int sh = 8 * (s & 3);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const uint4 b0 = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][16 * grp]);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(&bsm[buf][16 * m + col][64 + 16 * grp]);
-      const int sb = bsc[16 * m + col][s];
-      mfma4_fp4_fp8(acc[0][m], acc[1][m], acc[2][m], acc[3][m], a, b0, b1, sa[0], sa[1], sa[2],
-                    sa[3], sb);
+    for (int m = 0; m < MT; m += 2) {
+      v8i b[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 16 * (m + h) + col;
+        const v4i lo = *reinterpret_cast<const v4i*>(buf + t * 128 + 16 * tile_slot(t, grp));
+        const v4i hi = *reinterpret_cast<const v4i*>(buf + t * 128 + 16 * tile_slot(t, 4 + grp));
+        b[h] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      mfma8_fp4_fp8(acc[m], acc[m + 1], a, b[0], b[1], sa[0], sa[1], sa[2], sa[3],
+                    (int)(sbw[m] >> sh), (int)(sbw[m + 1] >> sh));
     }
   };
 
-  // S is even.  Loads past the last step re-read step S-1 (cache hits) so
-  // that the loop body has no conditional loads; each LDS buffer is written
-  // only after the barrier that follows the last read of it.
-  static_assert(S % 2 == 0, "even number of K steps");
-  load_a(0, A0);
-  load_a(1, A1);
-  load_st(0, ST);
-  store_st(st_dst0, ST);
-  __syncthreads();
-  load_st(1, ST);
-  for (int s = 0; s < S; s += 2) {
-    compute(s, 0, A0);                 // even step: ring slot A0, LDS buffer 0
-    load_a(min(s + 2, S - 1), A0);
-    store_st(st_dst1, ST);
-    __syncthreads();
-    load_st(min(s + 2, S - 1), ST);
-    compute(s + 1, 1, A1);             // odd step: ring slot A1, LDS buffer 1
-    load_a(min(s + 3, S - 1), A1);
-    store_st(st_dst0, ST);
-    __syncthreads();
-    load_st(min(s + 3, S - 1), ST);
+  // Pipeline, step s: barrier; activation loads for step s+2; compute(s)
+  // from buffer s%4 and ring slot s%4; weight loads for step s+4 into that
+  // slot; step s+1's activations (loaded during step s-1) written to buffer
+  // (s+1)%4, last read in step s-3.  Nothing past the last step is loaded.
+  uint8_t* const bufs[4] = {act0, act1, act2, act3};
+  load_a(0, A[0]);
+  stage_load(0, R[0]);
+  load_a(1, A[1]);
+  stage_load(1, R[1]);
+  load_a(2, A[2]);
+  load_a(3, A[3]);
+  stage_store(act0, R[0]);
+#define TILE_STEP(s, q)                                   \
+  do {                                                    \
+    lds_barrier();                                        \
+    if ((s) + 2 < S) stage_load((s) + 2, R[(q) & 1]);     \
+    compute((s), bufs[q], A[q]);                          \
+    if ((s) + 4 < S) load_a((s) + 4, A[q]);               \
+    if ((s) + 1 < S) stage_store(bufs[((q) + 1) & 3], R[((q) + 1) & 1]); \
+  } while (0)
+  for (int s0 = 0; s0 < S - 4; s0 += 4) {
+    TILE_STEP(s0, 0);
+    TILE_STEP(s0 + 1, 1);
+    TILE_STEP(s0 + 2, 2);
+    TILE_STEP(s0 + 3, 3);
   }
+  TILE_STEP(S - 4, 0);
+  TILE_STEP(S - 3, 1);
+  TILE_STEP(S - 2, 2);
+  TILE_STEP(S - 1, 3);
+#undef TILE_STEP
 
   if (MODE == 1) {
     // clamped SwiGLU, per-128 FP8 requant of h over this tile's 128 columns
@@ -716,10 +795,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float g = fminf(fmaxf(acc[tt][m][v], -lim), lim);
-          const float u = fminf(fmaxf(acc[tt + 2][m][v], -lim), lim);
+          const float g = fminf(fmaxf(acc[m][tt][v], -lim), lim);
+          const float u = fminf(fmaxf(acc[m][tt + 2][v], -lim), lim);
           const float hv = silu_f(g) * u;
-          acc[tt][m][v] = hv;                       // h kept in the w1 slots
+          acc[m][tt][v] = hv;                       // h kept in the w1 slots
           amax = fmaxf(amax, fabsf(hv));
         }
       amax = fmaxf(amax, __shfl_xor(amax, 16));
@@ -739,7 +818,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         for (int tt = 0; tt < 2; ++tt) {
           uint32_t word = 0;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(acc[tt][m][v], -ex)) << (8 * v);
+          for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(acc[m][tt][v], -ex)) << (8 * v);
           *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
         }
         if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
@@ -757,10 +836,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
         if (p.out_fp32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
-              make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+              make_float4(acc[m][t][0], acc[m][t][1], acc[m][t][2], acc[m][t][3]);
         } else {
-          const uint32_t lo = f32_to_bf16(acc[t][m][0]) | (f32_to_bf16(acc[t][m][1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[t][m][2]) | (f32_to_bf16(acc[t][m][3]) << 16);
+          const uint32_t lo = f32_to_bf16(acc[m][t][0]) | (f32_to_bf16(acc[m][t][1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[m][t][2]) | (f32_to_bf16(acc[m][t][3]) << 16);
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
               make_uint2(lo, hi);
         }
