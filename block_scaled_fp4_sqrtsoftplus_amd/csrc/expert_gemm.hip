@@ -24,13 +24,14 @@
 // So one K step is 128 elements: 64 weight bytes and 128 activation bytes
 // per row, and the FP8 activation block scale lines up with the step.
 //
-// Scale operands: the instruction reads its per-lane E8M0 scale registers
-// over several cycles after issue (measured: a scale register rewritten by
-// the very next VALU instruction gave rows 1-15 of the 16x16 tile the new
-// value, row 0 the old one), and the compiler neither holds such writes back
-// nor keeps a scale register untouched after its last use.  So the
-// instruction is issued from inline assembly followed by 32 wait states
-// (mfma_fp4_fp8 below), after which scale registers may be reused freely.
+// Scale operands: a streaming kernel built on the compiler builtin, whose
+// scale registers the compiler reused right after the MFMA, gave rows 1-15 of
+// the 16x16 tile a wrong scale (row 0 right).  Isolated probes that
+// overwrite an A, B or scale register with the very next VALU instruction
+// show no effect, so the exact condition is not pinned down; the kernels
+// therefore issue the instruction from inline assembly and keep its scale
+// registers and accumulators untouched for 32 wait states after it
+// (mfma_fp4_fp8 below, and once per K step in the tile kernel).
 //
 // Work decomposition: a workgroup (4 waves) owns one m-tile of one expert
 // (16 * MT pairs) and one n-tile of weight rows; it streams its weight rows
@@ -544,48 +545,145 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
 // ---------------------------------------------------------------------------
 // Tile variant for m-tiles of 128 pairs (prefill) when K is 1024, 2048 or
 // 4096.  Each of the four waves owns 4 weight tiles (64 rows) streamed into
-// registers through a four-step ring (each weight row's scale line read
-// once, as in the streaming kernel).  The 128 activation rows of a K step are
-// loaded two steps ahead into registers, written to one of four LDS buffers
-// at the end of the step before their use, and read by all four waves; the
-// 128 tokens' per-128 activation scales sit in LDS for the whole tile.  Per
-// K step a wave issues 32 MFMAs in four asm blocks of 8 (two 16-token
-// sub-tiles x four weight tiles), each closed by the wait states that
-// protect its operands.  Accumulators live in AGPRs.
+// registers through a four-step ring.  The 128 activation rows of a K step
+// are loaded two steps ahead into registers, written to one of four LDS
+// buffers at the end of the step before their use, and read by all four
+// waves.  The 128 tokens' per-128 activation scales and the 256 weight rows'
+// per-32 scale lines sit in LDS for the whole tile.  Per K step a wave
+// issues 32 MFMAs in four asm blocks of 8 (two 16-token sub-tiles x four
+// weight tiles); each block also reads the next block's activations from
+// LDS and waits for them.  The step's scale operands are computed before its
+// first block and held until its last block, which closes with the wait
+// states that protect them and the accumulators (one guard per step instead
+// of one per block).  Accumulators live in AGPRs.
 //
 // LDS activation layout: token t's 16-byte chunk c (bytes 16c..16c+15 of the
-// step) sits at slot c ^ (t & 7) ^ ((t >> 3) & 1) of the token's 128-byte
-// line, so that the 16-byte reads of 16 consecutive tokens (same c) hit
-// distinct banks.
+// step) sits at slot c ^ (t & 7) of the token's 128-byte line.  With that
+// xor the 16-byte reads of a wave (16 consecutive tokens x 4 chunks) run at
+// the LDS's full rate (measured on gfx950: about twice the rate of the
+// unswizzled and of other xor layouts).  For the reading lane (token
+// 16m + col, chunks grp and 4 + grp) the slot does not depend on m, and the
+// two chunks sit 64 bytes apart (xor), so every read of the step is one of
+// two per-lane base addresses plus an immediate offset
+// (buffer * 16384 + m * 2048).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int tile_slot(int t, int c) { return c ^ (t & 7) ^ ((t >> 3) & 1); }
+__device__ __forceinline__ int tile_slot(int t, int c) { return c ^ (t & 7); }
 
-// Two 16-token sub-tiles (B operands b0/b1, scales sb0/sb1) against four
-// weight tiles (a[0..3], scales sa0..sa3).
-__device__ __forceinline__ void mfma8_fp4_fp8(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
-                                              const v8i& b0, const v8i& b1, int sa0, int sa1,
-                                              int sa2, int sa3, int sb0, int sb1) {
-  asm(
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %12, %0, %14, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %9, %12, %1, %15, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %10, %12, %2, %16, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %11, %12, %3, %17, %18 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %8, %13, %4, %14, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %9, %13, %5, %15, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %10, %13, %6, %16, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %11, %13, %7, %17, %19 op_sel_hi:[0,0,0] cbsz:4\n\t"
+constexpr int kTileBuf = 128 * 128;   // bytes of one activation buffer
+
+#define TILE_MFMA8                                                                                 \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %[a0], %[b0], %0, %[s0], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %[a1], %[b0], %1, %[s1], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %[a2], %[b0], %2, %[s2], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %[a3], %[b0], %3, %[s3], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %[a0], %[b1], %4, %[s0], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %[a1], %[b1], %5, %[s1], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %[a2], %[b1], %6, %[s2], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %[a3], %[b1], %7, %[s3], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t"
+
+// Activations of two sub-tiles (tokens 16*m + col and 16*(m+1) + col) of the
+// buffer at byte offset BOFF: operand b = {chunk grp, chunk 4 + grp}.
+template <int OFF>
+__device__ __forceinline__ void tile_read2(v8i& b0, v8i& b1, uint32_t lo, uint32_t hi) {
+  v4i x0, x1, y0, y1;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n\t"
+      "ds_read_b128 %1, %5 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+      : "v"(lo), "v"(hi), "n"(OFF), "n"(OFF + 2048));
+  b0 = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  b1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+}
+
+// 8 MFMAs on (b0, b1) while reading the next two sub-tiles at OFF into
+// (n0, n1); the block ends once the reads have landed and 32 wait states
+// have passed since the last MFMA.
+// 8 MFMAs on (b0, b1) while reading the next two sub-tiles at OFF into
+// (n0, n1); the block ends once the reads have landed.  No wait states: the
+// caller keeps the scale registers and accumulators untouched until the
+// step's last block, which closes with them.
+template <int OFF>
+__device__ __forceinline__ void tile_mfma8_read(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+                                                const v8i& b0, const v8i& b1, const int (&sa)[4],
+                                                int sb0, int sb1, v8i& n0, v8i& n1, uint32_t lo,
+                                                uint32_t hi) {
+  v4i x0, x1, y0, y1;
+  asm volatile(
+      "ds_read_b128 %[x0], %[lo] offset:%[o0]\n\t"
+      "ds_read_b128 %[x1], %[hi] offset:%[o0]\n\t"
+      "ds_read_b128 %[y0], %[lo] offset:%[o1]\n\t"
+      "ds_read_b128 %[y1], %[hi] offset:%[o1]\n\t"
+      TILE_MFMA8
+      "s_waitcnt lgkmcnt(0)"
+      : "+a"(c0[0]), "+a"(c0[1]), "+a"(c0[2]), "+a"(c0[3]),
+        "+a"(c1[0]), "+a"(c1[1]), "+a"(c1[2]), "+a"(c1[3]),
+        [x0] "=&v"(x0), [x1] "=&v"(x1), [y0] "=&v"(y0), [y1] "=&v"(y1)
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0),
+        [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]),
+        [t0] "v"(sb0), [t1] "v"(sb1), [lo] "v"(lo), [hi] "v"(hi), [o0] "n"(OFF),
+        [o1] "n"(OFF + 2048));
+  n0 = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  n1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+}
+
+// The last 8 MFMAs of a step (sub-tiles 6, 7), closed by 32 wait states.
+// Also takes the step's other token scale registers (sb[0..5]) and the
+// previous block's activation operands (p0, p1), so that none of them is
+// reused before those wait states have passed.
+__device__ __forceinline__ void tile_mfma8_last(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+                                                const v8i& b0, const v8i& b1, const int (&sa)[4],
+                                                const int (&sb)[8], const v8i& p0, const v8i& p1) {
+  asm volatile(
+      TILE_MFMA8
       "s_nop 15\n\t"
       "s_nop 15"
       : "+a"(c0[0]), "+a"(c0[1]), "+a"(c0[2]), "+a"(c0[3]),
         "+a"(c1[0]), "+a"(c1[1]), "+a"(c1[2]), "+a"(c1[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b0), "v"(b1),
-        "v"(sa0), "v"(sa1), "v"(sa2), "v"(sa3), "v"(sb0), "v"(sb1));
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0),
+        [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]),
+        [t0] "v"(sb[6]), [t1] "v"(sb[7]), [k0] "v"(sb[0]), [k1] "v"(sb[1]), [k2] "v"(sb[2]),
+        [k3] "v"(sb[3]), [k4] "v"(sb[4]), [k5] "v"(sb[5]), [p0] "v"(p0), [p1] "v"(p1));
+}
+#undef TILE_MFMA8
+
+// Scales of a group of four K steps: the token scale dwords of the 8
+// sub-tiles (bytes s..s+3 of token 16*m + col's line: tok + m * TROW) and
+// the weight scale bytes 4s..4s+15 of the lane's row in each of the four
+// weight tiles (wrow + t * WROW).
+template <int TROW, int WROW>
+__device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4], uint32_t tok,
+                                                 uint32_t wrow) {
+  asm volatile(
+      "ds_read_b32 %0, %12\n\t"
+      "ds_read_b32 %1, %12 offset:%14\n\t"
+      "ds_read_b32 %2, %12 offset:%15\n\t"
+      "ds_read_b32 %3, %12 offset:%16\n\t"
+      "ds_read_b32 %4, %12 offset:%17\n\t"
+      "ds_read_b32 %5, %12 offset:%18\n\t"
+      "ds_read_b32 %6, %12 offset:%19\n\t"
+      "ds_read_b32 %7, %12 offset:%20\n\t"
+      "ds_read_b128 %8, %13\n\t"
+      "ds_read_b128 %9, %13 offset:%21\n\t"
+      "ds_read_b128 %10, %13 offset:%22\n\t"
+      "ds_read_b128 %11, %13 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(tw[0]), "=&v"(tw[1]), "=&v"(tw[2]), "=&v"(tw[3]), "=&v"(tw[4]), "=&v"(tw[5]),
+        "=&v"(tw[6]), "=&v"(tw[7]), "=&v"(ww[0]), "=&v"(ww[1]), "=&v"(ww[2]), "=&v"(ww[3])
+      : "v"(tok), "v"(wrow), "n"(TROW), "n"(2 * TROW), "n"(3 * TROW), "n"(4 * TROW),
+        "n"(5 * TROW), "n"(6 * TROW), "n"(7 * TROW), "n"(WROW), "n"(2 * WROW), "n"(3 * WROW));
 }
 
 // Workgroup barrier once this wave's LDS writes are done; no memory access
 // is moved across it (outstanding global loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 template <int MODE, int S>
@@ -595,12 +693,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   constexpr int K = S * 128;
   constexpr int SD = S / 4;
   static_assert(S % 4 == 0 && S >= 8, "K steps in groups of four, at least two groups");
-  // four activation buffers (one per step of a group of four)
-  __shared__ __attribute__((aligned(1024))) uint8_t act0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t act1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t act2[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t act3[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t act[4 * kTileBuf];
+  constexpr int WLINE = 4 * S + 16;     // weight scale line, padded (banks)
   __shared__ __attribute__((aligned(16))) uint8_t bsc[BM][S];
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[4][64][WLINE];
   __shared__ float red[4][BM];
   (void)mt_max;
 
@@ -616,6 +712,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   const size_t wrow_bytes = (size_t)K / 2;
   const size_t srow_bytes = (size_t)K / 32;
 
+  // weight rows of this wave (waves past N in GEMM2 read row 0 and skip the
+  // MFMAs: unconditional loads keep every wave's load count the same)
   const uint8_t* wptr[4];
   const uint8_t* sptr[4];
   int n0;
@@ -651,8 +749,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 
   // Activation staging: this thread moves 4 x 16 bytes per step, for tokens
   // 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the token's
-  // line, i.e. chunk slot ^ (t & 7) ^ ((t >> 3) & 1) of the step (the map is
-  // an involution on the chunk index)
+  // line, i.e. chunk tile_slot(t, lane%8) of the step (the map is an
+  // involution on the chunk index)
   const uint8_t* ssrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -665,9 +763,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const v4i*>(ssrc[j] + (size_t)s * 128);
   };
-  auto stage_store = [&](uint8_t* buf, const v4i (&r)[4]) {
+  auto stage_store = [&](int q, const v4i (&r)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(buf + sdst + 1024 * j) = r[j];
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<v4i*>(act + q * kTileBuf + sdst + 1024 * j) = r[j];
   };
 
   // token scales of the whole tile into LDS: thread tid copies half of
@@ -685,22 +784,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     }
   }
 
-  // weight scale lines (a quarter per lane group)
-  uint32_t SR[4][SD];
-  {
+  // weight scale lines into LDS (a quarter per lane group): row 16*t + col
+  // of this wave's 64
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint8_t* src = sptr[t] + grp * S;
-      if constexpr (SD >= 4) {
+  for (int t = 0; t < 4; ++t) {
+    const uint8_t* src = sptr[t] + grp * S;
+    uint8_t* dst = &wsc[wv][16 * t + col][grp * S];
+    if constexpr (S >= 16) {
 #pragma unroll
-        for (int j = 0; j < SD / 4; ++j) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * j);
-          SR[t][4 * j] = v.x; SR[t][4 * j + 1] = v.y; SR[t][4 * j + 2] = v.z; SR[t][4 * j + 3] = v.w;
-        }
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        SR[t][0] = v.x; SR[t][1] = v.y;
-      }
+      for (int j = 0; j < S / 16; ++j)
+        reinterpret_cast<uint4*>(dst)[j] = reinterpret_cast<const uint4*>(src)[j];
+    } else {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
     }
   }
 
@@ -711,79 +806,92 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     for (int t = 0; t < 4; ++t) acc[m][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   v4i A[4][4];  // weight ring: [step % 4][tile]
-  // (waves without weight rows load row 0 too: unconditional loads keep the
-  // compiler's load counting exact)
   auto load_a = [&](int s, v4i (&a)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4i*>(wptr[t] + (size_t)s * 64);
   };
 
-  // one K step: activations from `buf`, weights from ring slot `a`; the
-  // four steps of a group share one dword of token scales per sub-tile
+  // per-lane LDS addresses
+  const int rslot = tile_slot(col, grp);
+  const uint32_t rd_lo = lds_addr(act) + col * 128 + 16 * rslot;
+  const uint32_t rd_hi = rd_lo ^ 64u;
+  const uint32_t sc_tok = lds_addr(&bsc[col][0]);
+  const uint32_t sc_w = lds_addr(&wsc[wv][col][0]);
+
   uint32_t sbw[MT];
-  auto compute = [&](int s, const uint8_t* buf, const v4i (&a)[4]) {
+  v4i saw[4];
+  // one K step from buffer Q (compile-time) and ring slot Q
+  auto compute = [&](int s, auto qc) {
+    constexpr int Q = decltype(qc)::value;
     if (!wave_live) return;
-    if ((s & 3) == 0) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        sbw[m] = *reinterpret_cast<const uint32_t*>(&bsc[16 * m + col][s]);
-    }
-    const int src_lane = col + 16 * (s / SD);
-    int sa[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t w = SR[t][0];
-#pragma unroll
-      for (int j = 1; j < SD; ++j) w = ((s & (SD - 1)) == j) ? SR[t][j] : w;
-      sa[t] = __shfl((int)w, src_lane) >> (8 * grp);
-    }
-    const int sh = 8 * (s & 3);
-#pragma unroll
-    for (int m = 0; m < MT; m += 2) {
-      v8i b[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 16 * (m + h) + col;
-        const v4i lo = *reinterpret_cast<const v4i*>(buf + t * 128 + 16 * tile_slot(t, grp));
-        const v4i hi = *reinterpret_cast<const v4i*>(buf + t * 128 + 16 * tile_slot(t, 4 + grp));
-        b[h] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      mfma8_fp4_fp8(acc[m], acc[m + 1], a, b[0], b[1], sa[0], sa[1], sa[2], sa[3],
-                    (int)(sbw[m] >> sh), (int)(sbw[m + 1] >> sh));
-    }
+    if (Q == 0) tile_read_scales<16 * S, 16 * WLINE>(sbw, saw, sc_tok + s, sc_w + 4 * s);
+    const int sa[4] = {saw[0][Q] >> (8 * grp), saw[1][Q] >> (8 * grp), saw[2][Q] >> (8 * grp),
+                       saw[3][Q] >> (8 * grp)};
+    const int sh = 8 * Q;
+    const int sb[8] = {(int)(sbw[0] >> sh), (int)(sbw[1] >> sh), (int)(sbw[2] >> sh),
+                       (int)(sbw[3] >> sh), (int)(sbw[4] >> sh), (int)(sbw[5] >> sh),
+                       (int)(sbw[6] >> sh), (int)(sbw[7] >> sh)};
+    constexpr int B = Q * kTileBuf;
+    v8i x0, x1, y0, y1;
+    // one guard per step: every scale register of the step stays live until
+    // the last block, which closes with the wait states
+    tile_read2<B>(x0, x1, rd_lo, rd_hi);
+    tile_mfma8_read<B + 2 * 2048>(acc[0], acc[1], A[Q], x0, x1, sa, sb[0], sb[1], y0,
+                                               y1, rd_lo, rd_hi);
+    tile_mfma8_read<B + 4 * 2048>(acc[2], acc[3], A[Q], y0, y1, sa, sb[2], sb[3], x0,
+                                               x1, rd_lo, rd_hi);
+    tile_mfma8_read<B + 6 * 2048>(acc[4], acc[5], A[Q], x0, x1, sa, sb[4], sb[5], y0,
+                                               y1, rd_lo, rd_hi);
+    tile_mfma8_last(acc[6], acc[7], A[Q], y0, y1, sa, sb, x0, x1);
   };
 
   // Pipeline, step s: barrier; activation loads for step s+2; compute(s)
   // from buffer s%4 and ring slot s%4; weight loads for step s+4 into that
   // slot; step s+1's activations (loaded during step s-1) written to buffer
   // (s+1)%4, last read in step s-3.  Nothing past the last step is loaded.
-  uint8_t* const bufs[4] = {act0, act1, act2, act3};
   load_a(0, A[0]);
   stage_load(0, R[0]);
   load_a(1, A[1]);
   stage_load(1, R[1]);
   load_a(2, A[2]);
   load_a(3, A[3]);
-  stage_store(act0, R[0]);
-#define TILE_STEP(s, q)                                   \
-  do {                                                    \
-    lds_barrier();                                        \
-    if ((s) + 2 < S) stage_load((s) + 2, R[(q) & 1]);     \
-    compute((s), bufs[q], A[q]);                          \
-    if ((s) + 4 < S) load_a((s) + 4, A[q]);               \
-    if ((s) + 1 < S) stage_store(bufs[((q) + 1) & 3], R[((q) + 1) & 1]); \
+  stage_store(0, R[0]);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+#define TILE_STEP(s, QC)                                          \
+  do {                                                            \
+    constexpr int q_ = QC::value;                                 \
+    lds_barrier();                                                \
+    if ((s) + 2 < S) stage_load((s) + 2, R[q_ & 1]);              \
+    compute((s), QC{});                                           \
+    if ((s) + 4 < S) load_a((s) + 4, A[q_]);                      \
+    if ((s) + 1 < S) stage_store((q_ + 1) & 3, R[(q_ + 1) & 1]);  \
   } while (0)
   for (int s0 = 0; s0 < S - 4; s0 += 4) {
-    TILE_STEP(s0, 0);
-    TILE_STEP(s0 + 1, 1);
-    TILE_STEP(s0 + 2, 2);
-    TILE_STEP(s0 + 3, 3);
+    TILE_STEP(s0, I0);
+    TILE_STEP(s0 + 1, I1);
+    TILE_STEP(s0 + 2, I2);
+    TILE_STEP(s0 + 3, I3);
   }
-  TILE_STEP(S - 4, 0);
-  TILE_STEP(S - 3, 1);
-  TILE_STEP(S - 2, 2);
-  TILE_STEP(S - 1, 3);
+  TILE_STEP(S - 4, I0);
+  TILE_STEP(S - 3, I1);
+  TILE_STEP(S - 2, I2);
+  TILE_STEP(S - 1, I3);
 #undef TILE_STEP
+  // the epilogue reads the accumulators only after the last block's wait
+  // states (the MFMAs are invisible to the compiler's hazard tracking)
+  asm volatile(""
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                 "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+  asm volatile(""
+               : "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]), "+a"(acc[4][3]),
+                 "+a"(acc[5][0]), "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]),
+                 "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3]),
+                 "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]));
 
   if (MODE == 1) {
     // clamped SwiGLU, per-128 FP8 requant of h over this tile's 128 columns

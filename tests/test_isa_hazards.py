@@ -1,10 +1,15 @@
-"""The gfx950 scaled MFMA reads its operand registers (notably the per-lane
-E8M0 scale registers) for several cycles after issue, and the compiler does
-not keep those registers untouched afterwards.  The expert GEMMs therefore
-issue it from inline assembly followed by 32 wait states.  This test builds
-the GEMM source for gfx950 and checks, in the generated AMD assembly, that no
-instruction writes an operand register of a scaled MFMA within 32 wait
-states of it.  CPU-only: hipcc cross-compiles."""
+"""The expert GEMMs issue the gfx950 scaled MFMA from inline assembly and
+close each group of MFMAs with 32 wait states, so that no later instruction
+overwrites a register the MFMA may still read: the compiler does not see the
+MFMA inside the asm and would not hold such writes back.  (A streaming GEMM
+that let the compiler reuse a per-lane E8M0 scale register right after the
+MFMA produced wrong rows; overwriting the A or B data registers with the
+next VALU instruction has been measured harmless on gfx950.)  This test
+builds the GEMM source for gfx950 and checks, in the generated AMD assembly,
+that no VALU instruction writes a scale register or the accumulator of a
+scaled MFMA within 32 wait states of it, and that nothing but another MFMA
+reads an MFMA's accumulator within that distance.  CPU-only: hipcc
+cross-compiles."""
 
 import os
 import re
@@ -59,7 +64,7 @@ def test_scaled_mfma_operands_untouched_for_32_wait_states():
                 continue
             total += 1
             ops = [o.strip() for o in s.split(None, 1)[1].split(" op_sel")[0].split(",")]
-            watch = _regs(ops[1]) | _regs(ops[2]) | _regs(ops[4]) | _regs(ops[5])
+            watch = _regs(ops[0]) | _regs(ops[4]) | _regs(ops[5])
             ws = 0
             for t in ins[i + 1:]:
                 if ws >= NEED:
@@ -73,6 +78,10 @@ def test_scaled_mfma_operands_untouched_for_32_wait_states():
                     continue
                 parts = t.split(None, 1)
                 if len(parts) == 2:
-                    dst = parts[1].split(",")[0].strip()
-                    assert not (_regs(dst) & watch), f"{name}: '{t}' {ws} wait states after '{s}'"
+                    args = [a.strip() for a in parts[1].split(",")]
+                    assert not (_regs(args[0]) & watch), f"{name}: '{t}' {ws} wait states after '{s}'"
+                    if not t.startswith("v_mfma"):
+                        # no read of the accumulator before the result is final
+                        read = set().union(*(_regs(a.split()[0]) for a in args[1:] if a))
+                        assert not (read & _regs(ops[0])), f"{name}: '{t}' reads the result {ws} wait states after '{s}'"
     assert total > 0
