@@ -20,6 +20,7 @@ namespace moe {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
 
@@ -352,11 +353,163 @@ __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M tile kernel: 128 tokens x 128 weight rows per workgroup, K in steps
+// of 64.  Both operands go through double-buffered LDS (each row's 128-byte
+// step line with its 16-byte chunk c at slot c ^ (row & 7), so that the
+// 16-byte operand reads of 16 consecutive rows hit distinct banks); the four
+// waves split the tile 2 x 2 (64 tokens x 64 rows each, 32 MFMAs per step).
+// The next step's lines are loaded into registers at the start of a step
+// and written to the other buffer at its end; one barrier per step.
+//   EPI_F32    rows n0..n0+127 of W, out[t][n] fp32
+//   EPI_SWIGLU LDS rows 0..63 = w1 rows c0..c0+63, rows 64..127 = w3 rows of
+//              the same columns; wave (wm, wn) takes columns c0 + 32 wn ..
+//              +31 of both, so g and u of an output meet in one lane.
+// Requires N % 128 == 0 (EPI_F32) or N % 64 == 0 (EPI_SWIGLU), K % 64 == 0.
+// ---------------------------------------------------------------------------
+constexpr int kBfTileLine = 128;            // bytes of a row's K step (64 bf16)
+constexpr int kBfTileBuf = 128 * kBfTileLine;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ W,
+                                                           const uint16_t* __restrict__ W3,
+                                                           void* __restrict__ out, int64_t M, int N,
+                                                           int K, float limit) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As[2][kBfTileBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kBfTileBuf];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * 128;
+  const int nb = blockIdx.x;
+  const size_t row_bytes = (size_t)K * 2;
+
+  // staging: thread tid moves chunks 4h..4h+3 of row r (r = tid % 128,
+  // h = tid / 128) of both operands, chunk c to slot c ^ (r & 7)
+  const int sr = tid & 127, sh = tid >> 7;
+  const uint8_t* wsrc;
+  if (EPI == EPI_SWIGLU) {
+    const int c = nb * 64 + (sr & 63);
+    wsrc = reinterpret_cast<const uint8_t*>(sr < 64 ? W : W3) + (size_t)c * row_bytes;
+  } else {
+    wsrc = reinterpret_cast<const uint8_t*>(W) + (size_t)(nb * 128 + sr) * row_bytes;
+  }
+  const int64_t xr = m0 + sr < M ? m0 + sr : M - 1;   // rows past M repeat row M-1 (dropped)
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(X) + (size_t)xr * row_bytes;
+  uint32_t soff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) soff[j] = sr * kBfTileLine + 16 * ((4 * sh + j) ^ (sr & 7));
+  // (native vector types: loops of struct copies would go through memory)
+  v4i ga[4], gb[4];
+  auto gload = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ga[j] = *reinterpret_cast<const v4i*>(wsrc + (size_t)s * kBfTileLine + 16 * (4 * sh + j));
+      gb[j] = *reinterpret_cast<const v4i*>(xsrc + (size_t)s * kBfTileLine + 16 * (4 * sh + j));
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<v4i*>(&As[buf][soff[j]]) = ga[j];
+      *reinterpret_cast<v4i*>(&Bs[buf][soff[j]]) = gb[j];
+    }
+  };
+
+  // operand rows of this wave in the LDS tile
+  int arow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    arow[t] = EPI == EPI_SWIGLU ? (t < 2 ? 32 * wn + 16 * t : 64 + 32 * wn + 16 * (t - 2))
+                                : 64 * wn + 16 * t;
+  const int lo = 16 * (grp ^ (col & 7));      // chunk grp of a row line (row & 7 == col & 7)
+  const int hi = lo ^ 64;                     // chunk grp + 4
+
+  v4f acc[4][4];   // [weight tile][token sub-tile]
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = K / 64;
+  gload(0);
+  lstore(0);
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    __syncthreads();                  // buffer buf written, buffer buf^1 free
+    if (s + 1 < steps) gload(s + 1);
+    bf16x8 a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* r = &As[buf][(arow[t] + col) * kBfTileLine];
+      a0[t] = *reinterpret_cast<const bf16x8*>(r + lo);
+      a1[t] = *reinterpret_cast<const bf16x8*>(r + hi);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* r = &Bs[buf][(64 * wm + 16 * m + col) * kBfTileLine];
+      b0[m] = *reinterpret_cast<const bf16x8*>(r + lo);
+      b1[m] = *reinterpret_cast<const bf16x8*>(r + hi);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[t], b0[m], acc[t][m], 0, 0, 0);
+        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[t], b1[m], acc[t][m], 0, 0, 0);
+      }
+    if (s + 1 < steps) lstore(buf ^ 1);
+  }
+
+  // D layout: lane l holds D[4*(l/16)+v][l%16] = C[token l%16][row 4*(l/16)+v]
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int64_t r = m0 + 64 * wm + 16 * m + col;
+    if (r >= M) continue;
+    if (EPI == EPI_F32) {
+      float* o = static_cast<float*>(out) + (size_t)r * N;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = nb * 128 + 64 * wn + 16 * t + 4 * grp;
+        *reinterpret_cast<float4*>(o + c) =
+            make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+      }
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)r * N;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = nb * 64 + 32 * wn + 16 * t + 4 * grp;
+        uint32_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g = fminf(fmaxf(acc[t][m][v], -limit), limit);
+          const float u = fminf(fmaxf(acc[t + 2][m][v], -limit), limit);
+          hv[v] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        }
+        *reinterpret_cast<uint2*>(o + c) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
+    }
+  }
+}
+
+// tokens from which the tile kernel is used
+constexpr int64_t kBfTileMinM = 256;
+
 template <int EPI, int TPW>
 static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* W3, void* out,
                               int64_t M, int N, int K, float limit, hipStream_t st) {
   if (M == 0) return hipSuccess;
   if (M <= 64 && K % 1024 == 0) return launch_skinny<EPI>(X, W, W3, out, (int)M, N, K, limit, st);
+  if (M >= kBfTileMinM && K % 64 == 0 && N % (EPI == EPI_SWIGLU ? 64 : 128) == 0) {
+    const dim3 grid((unsigned)(N / (EPI == EPI_SWIGLU ? 64 : 128)), (unsigned)((M + 127) / 128));
+    hipLaunchKernelGGL((bf16_tile_kernel<EPI>), grid, dim3(256), 0, st, X, W, W3, out, M, N, K,
+                       limit);
+    return hipGetLastError();
+  }
   constexpr int WROWS = EPI == EPI_SWIGLU ? 8 * TPW : 16 * TPW;
   const unsigned gx = (unsigned)((N + 4 * WROWS - 1) / (4 * WROWS));
   if (M <= 16) {
