@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="report graph replays of the layer (moe_graph_launch) as the step; "
+                         "both are timed and reported either way")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -139,20 +142,27 @@ def main():
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {wl}", file=sys.stderr, flush=True)
 
-    # ---- whole layer ----
-    for _ in range(args.warmup):
-        L(x, ids, y=y, routing=routing)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
-        L(x, ids, y=y, routing=routing)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_step = wall * 1e3 / steps
-    gpu_ms_step = ev0.elapsed_time(ev1) / steps
+    # ---- whole layer: eager calls (the step that sets `value`), then replays
+    # of the same call captured into a HIP graph (sets `value` with --graph) ----
+    def timed(step_fn):
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start = time.perf_counter()
+        ev0.record()
+        for _ in range(steps):
+            step_fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_start) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+    eager_ms, eager_gpu_ms = timed(lambda: L(x, ids, y=y, routing=routing))
+    graph = moe.LayerGraph(L, x, token_ids=ids, y=y, routing=routing)
+    graph_ms, graph_gpu_ms = timed(graph.launch)
+    graph.close()
+    launch = "graph" if args.graph else "eager"
+    ms_step, gpu_ms_step = (graph_ms, graph_gpu_ms) if args.graph else (eager_ms, eager_gpu_ms)
     n_touched = int(np.sum(np.diff(routing["expert_offsets"].cpu().numpy()) > 0))
     load = np.diff(routing["expert_offsets"].cpu().numpy())
 
@@ -194,7 +204,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
-    roof["kernel"] = "routed expert FFN: expert_gemm_kernel<1> + <2> (+ tile prefix)"
+    fam = "expert_gemm_stream" if wl.tokens * wl.top_k <= 32 * wl.n_experts else "expert_gemm_tile"
+    roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
+                      " (+ tile prefix)")
     roof["ms_per_call"] = round(ffn_ms, 4)
     roof["alg_bytes_per_call"] = alg["ffn_bytes"]
     roof["alg_flops_per_call"] = alg["flops_routed"]
@@ -233,7 +245,10 @@ def main():
                                f"{' + bf16 shared expert' if wl.shared else ''}",
                    "tokens": wl.tokens, "experts_touched": n_touched,
                    "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2)},
-        "layer": {"gpu_ms_per_step": round(gpu_ms_step, 4),
+        "layer": {"launch": launch,
+                  "gpu_ms_per_step": round(gpu_ms_step, 4),
+                  "eager_ms_per_step": round(eager_ms, 4),
+                  "graph_ms_per_step": round(graph_ms, 4),
                   "alg_bytes": alg["layer_bytes"],
                   "hbm_gbs": round(alg["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1),
                   "roofline_frac": round(layer_t_roof / (ms_step * 1e-3), 4)},

@@ -70,6 +70,16 @@ lib.moe_layer.restype = ctypes.c_int
 lib.moe_layer.argtypes = [ctypes.POINTER(MoeConfigC), _vp, _vp, _vp, _vp,
                           ctypes.POINTER(MoeExpertWeightsC), ctypes.POINTER(MoeSharedWeightsC), _vp,
                           ctypes.POINTER(MoeRoutingC), _vp, _sz, _vp]
+lib.moe_layer_graph_create.restype = ctypes.c_int
+lib.moe_layer_graph_create.argtypes = [ctypes.POINTER(MoeConfigC), _vp, _vp, _vp, _vp,
+                                       ctypes.POINTER(MoeExpertWeightsC),
+                                       ctypes.POINTER(MoeSharedWeightsC), _vp,
+                                       ctypes.POINTER(MoeRoutingC), _vp, _sz,
+                                       ctypes.POINTER(_vp)]
+lib.moe_graph_launch.restype = ctypes.c_int
+lib.moe_graph_launch.argtypes = [_vp, _vp]
+lib.moe_graph_destroy.restype = ctypes.c_int
+lib.moe_graph_destroy.argtypes = [_vp]
 
 
 class MoeError(RuntimeError):
@@ -224,6 +234,42 @@ class Layer:
                              _ptr(y), ctypes.byref(rc) if rc is not None else None,
                              _ptr(self.ws), self.ws_bytes, _stream()))
         return y
+
+
+class LayerGraph:
+    """One moe_layer call recorded into a HIP graph (moe_layer_graph_create)
+    with fixed buffers: update x (and token_ids) in place, then launch();
+    y and the routing arrays receive the results.  Holds references to every
+    buffer the graph reads or writes."""
+
+    def __init__(self, layer: "Layer", x, token_ids=None, y=None, routing=None):
+        cfg = layer.cfg
+        if y is None:
+            y = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device=layer.device)
+        self.layer, self.x, self.token_ids, self.y, self.routing = layer, x, token_ids, y, routing
+        rc = _routing_c(routing) if routing is not None else None
+        h = _vp()
+        _check(lib.moe_layer_graph_create(
+            ctypes.byref(layer._c), _ptr(x), _ptr(layer.w_gate), _ptr(layer.bias), _ptr(token_ids),
+            ctypes.byref(layer._wc), ctypes.byref(layer._sc) if layer._sc is not None else None,
+            _ptr(y), ctypes.byref(rc) if rc is not None else None, _ptr(layer.ws), layer.ws_bytes,
+            ctypes.byref(h)))
+        self._h = h
+
+    def launch(self):
+        _check(lib.moe_graph_launch(self._h, _stream()))
+        return self.y
+
+    def close(self):
+        if self._h:
+            _check(lib.moe_graph_destroy(self._h))
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def layer(cfg: Config, x, weights, w_gate=None, bias=None, token_ids=None, shared=None,

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <new>
 
 #include "moe_internal.h"
 
@@ -376,10 +377,15 @@ moe_status moe_expert_ffn(const moe_config* cfg, const uint8_t* xq, const uint8_
                      static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
-                     const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
-                     const moe_shared_weights* shared, uint16_t* y,
-                     const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_layer (and of its graph capture), host-side only.
+moe_status layer_check(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                       const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
+                       const moe_shared_weights* shared, const uint16_t* y,
+                       const moe_routing* routing_out, const void* ws, size_t ws_bytes) {
   moe_status s = check_cfg(cfg);
   if (s != MOE_OK) return s;
   const moe_config& c = *cfg;
@@ -404,7 +410,22 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (need && !ws) return MOE_ERR_NULL_ARG;
   if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                     const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
+                     const moe_shared_weights* shared, uint16_t* y,
+                     const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = layer_check(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws,
+                             ws_bytes);
+  if (s != MOE_OK) return s;
   if ((s = check_device()) != MOE_OK) return s;
+  const moe_config& c = *cfg;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
@@ -444,6 +465,58 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   if (shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
   MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, y, c.tokens, c.hidden, c.top_k, st));
   return MOE_OK;
+}
+
+struct moe_graph {
+  hipGraphExec_t exec;
+};
+
+moe_status moe_layer_graph_create(const moe_config* cfg, const uint16_t* x,
+                                  const uint16_t* w_gate, const float* bias,
+                                  const int64_t* token_ids, const moe_expert_weights* w,
+                                  const moe_shared_weights* shared, uint16_t* y,
+                                  const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                                  moe_graph** graph_out) {
+  if (!graph_out) return MOE_ERR_NULL_ARG;
+  *graph_out = nullptr;
+  moe_status s = layer_check(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws,
+                             ws_bytes);
+  if (s != MOE_OK) return s;
+  if ((s = check_device()) != MOE_OK) return s;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return MOE_ERR_HIP;
+  }
+  s = moe_layer(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws, ws_bytes, cs);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(cs, &g);
+  if (s == MOE_OK && (ec != hipSuccess || !g)) s = MOE_ERR_HIP;
+  hipGraphExec_t ge = nullptr;
+  if (s == MOE_OK && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) s = MOE_ERR_HIP;
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (s != MOE_OK) return s;
+  moe_graph* h = new (std::nothrow) moe_graph{ge};
+  if (!h) {
+    (void)hipGraphExecDestroy(ge);
+    return MOE_ERR_HIP;
+  }
+  *graph_out = h;
+  return MOE_OK;
+}
+
+moe_status moe_graph_launch(const moe_graph* graph, void* stream) {
+  if (!graph) return MOE_ERR_NULL_ARG;
+  return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_graph_destroy(moe_graph* graph) {
+  if (!graph) return MOE_OK;
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -201,6 +201,28 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
                      const moe_shared_weights* shared, uint16_t* y,
                      const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Graph replay of the layer ("DeepSeek-V4-Flash-SI" card, 模型推理 /
+ * 推理模式: the MoE GEMM path captured into a graph to cut kernel-launch
+ * overhead; 模型效果 / 质量标准: graph output identical to eager).
+ * moe_layer_graph_create records one moe_layer call (same arguments, no
+ * stream) into a HIP graph on a private stream and instantiates it; every
+ * pointer, the config and the shared/routing structs' contents are baked in.
+ * moe_graph_launch replays it on `stream`: the caller updates x (and any
+ * inputs) in place between replays and keeps every buffer, the weights and
+ * `ws` alive until moe_graph_destroy.  Replays of one graph must not overlap
+ * each other or an eager call on the same workspace.  The graph contains no
+ * memset nodes.  Errors: those of moe_layer (nothing is created), or
+ * MOE_ERR_HIP if capture or instantiation fails; *graph_out is NULL then. */
+typedef struct moe_graph moe_graph;
+moe_status moe_layer_graph_create(const moe_config* cfg, const uint16_t* x,
+                                  const uint16_t* w_gate, const float* bias,
+                                  const int64_t* token_ids, const moe_expert_weights* w,
+                                  const moe_shared_weights* shared, uint16_t* y,
+                                  const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                                  moe_graph** graph_out);
+moe_status moe_graph_launch(const moe_graph* graph, void* stream);
+moe_status moe_graph_destroy(moe_graph* graph);   /* NULL is a no-op */
+
 #ifdef __cplusplus
 }
 #endif

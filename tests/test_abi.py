@@ -25,7 +25,8 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_quant_act", "moe_route",
-                          "moe_expert_ffn", "moe_layer"}
+                          "moe_expert_ffn", "moe_layer", "moe_layer_graph_create",
+                          "moe_graph_launch", "moe_graph_destroy"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +104,27 @@ def test_layer_argument_errors():
     # incomplete routing_out
     r = moe.MoeRoutingC(16, 16, None, 16, 16)
     assert lib.moe_layer(ctypes.byref(c), 16, 16, None, None, ctypes.byref(w), None, 16, ctypes.byref(r), 16, big, None) == 1
+
+
+def test_graph_argument_errors():
+    c = _cfg()
+    big = 1 << 40
+    w = _w()
+    h = ctypes.c_void_p(12345)
+    # no place for the handle
+    assert lib.moe_layer_graph_create(ctypes.byref(c), 16, 16, None, None, ctypes.byref(w), None, 16,
+                                      None, 16, big, None) == 1
+    # the layer's own argument errors, before any HIP call; the handle is cleared
+    assert lib.moe_layer_graph_create(ctypes.byref(c), None, 16, None, None, ctypes.byref(w), None,
+                                      16, None, 16, big, ctypes.byref(h)) == 1
+    assert not h.value
+    assert lib.moe_layer_graph_create(ctypes.byref(c), 18, 16, None, None, ctypes.byref(w), None,
+                                      16, None, 16, big, ctypes.byref(h)) == 3
+    need = lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER)
+    assert lib.moe_layer_graph_create(ctypes.byref(c), 16, 16, None, None, ctypes.byref(w), None,
+                                      16, None, 16, need - 1, ctypes.byref(h)) == 4
+    assert lib.moe_graph_launch(None, None) == 1
+    assert lib.moe_graph_destroy(None) == 0
 
 
 def test_quant_act_argument_errors():

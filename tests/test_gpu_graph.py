@@ -1,0 +1,66 @@
+"""Graph replay of the whole layer (moe_layer_graph_create / moe_graph_launch)
+against eager moe_layer calls: every replay must give bit-identical outputs
+and routing ("DeepSeek-V4-Flash-SI" card, 模型效果 / 质量标准: graph decoding
+identical to eager).  Replays are interleaved with eager work on the same
+device and with in-place updates of x, and each replay is checked."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import config, device_inputs
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("block_scaled_fp4_sqrtsoftplus_amd")
+
+
+def _setup(name, tokens, **over):
+    wl = synth.WORKLOADS[name].replace(**over)
+    inp = synth.make_inputs(wl, tokens=tokens)
+    d = device_inputs(inp)
+    T = inp["x"].shape[0]
+    cfg = config(moe, wl, tokens=T)
+    L = moe.Layer(cfg, d["weights"], w_gate=d["w_gate"], bias=d["bias"], shared=d["shared"])
+    return wl, inp, d, L
+
+
+def _eager(L, x, ids, cfg):
+    y = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device=x.device)
+    r = moe._routing_tensors(cfg.tokens, cfg.top_k, cfg.n_experts, x.device)
+    L(x, ids, y=y, routing=r)
+    return y, r
+
+
+@pytest.mark.parametrize("name,tokens,over", [
+    ("decode", None, {}),                                                   # full decode shape
+    ("tiny", 40, dict(hidden=512, inter=256, n_experts=12, top_k=3, shared=True)),
+    ("tiny", 33, dict(mode="hash", n_experts=20, top_k=6, hidden=384, inter=256, shared=True)),
+])
+def test_graph_replays_match_eager(name, tokens, over):
+    wl, inp, d, L = _setup(name, tokens, **over)
+    cfg = L.cfg
+    x = d["x"].clone()
+    ids = d["token_ids"]
+    y_ref, r_ref = _eager(L, x, ids, cfg)
+    x2 = torch.roll(d["x"], shifts=1, dims=0).contiguous()       # a second batch
+    y2_ref, r2_ref = _eager(L, x2, ids, cfg)
+    torch.cuda.synchronize()
+
+    g_routing = moe._routing_tensors(cfg.tokens, cfg.top_k, cfg.n_experts, x.device)
+    g = moe.LayerGraph(L, x, token_ids=ids, routing=g_routing)
+    try:
+        for it in range(4):
+            use2 = it % 2 == 1
+            x.copy_(x2 if use2 else d["x"])          # in-place input update
+            yg = g.launch()
+            # eager work between replays: another layer call on other buffers
+            _eager(L, x2 if not use2 else d["x"], ids, cfg)
+            torch.cuda.synchronize()
+            want_y, want_r = (y2_ref, r2_ref) if use2 else (y_ref, r_ref)
+            assert torch.equal(yg.view(torch.int16), want_y.view(torch.int16)), f"replay {it}: y differs"
+            for k in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_pos"):
+                assert torch.equal(g_routing[k], want_r[k]), f"replay {it}: {k} differs"
+    finally:
+        g.close()
