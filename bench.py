@@ -35,17 +35,21 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="report graph replays of the layer (moe_graph_launch) as the step; "
                          "both are timed and reported either way")
+    ap.add_argument("--experts", choices=("mxfp4", "fp8"), default="mxfp4",
+                    help="routed expert weights: the MXFP4 checkpoint format, or its "
+                         "per-128 cast to FP8 (made on the GPU before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
-def algorithmic(wl, n_touched):
+def algorithmic(wl, n_touched, fp8=False):
     """Bytes and flops the layer must move / compute (no padding, no
     intermediates): weights of the touched experts (FP4 nibbles + E8M0
-    scales of w1, w3, w2), the bf16 shared expert and gate, x in, y out."""
+    scales per 32 of w1, w3, w2; FP8 experts: E4M3 bytes + E8M0 per 128),
+    the bf16 shared expert and gate, x in, y out."""
     T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.n_experts, wl.top_k
-    per_expert = 3 * (I * H // 2 + I * H // 32)
+    per_expert = 3 * (I * H + I * H // 128) if fp8 else 3 * (I * H // 2 + I * H // 32)
     ffn_bytes = n_touched * per_expert + T * (H + H // 128) + T * k * H * 4
     shared = 3 * I * H * 2 if wl.shared else 0
     gate = E * H * 2 if wl.mode != "hash" else 0
@@ -70,7 +74,7 @@ def traffic_record(kernel_src_hash, workload):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(wl, inp, budget_s=20.0):
+def cpu_baseline(wl, inp, budget_s=20.0, weight_format="mxfp4"):
     """The oracle as it stands on a bounded token sample: as many tokens of
     the workload as fit in about budget_s seconds (at least one)."""
     import numpy as np
@@ -89,7 +93,8 @@ def cpu_baseline(wl, inp, budget_s=20.0):
         sub["x"] = inp["x"][S]
         sub["token_ids"] = inp["token_ids"][S]
         t0 = time.perf_counter()
-        ffn.layer(sub, wl.top_k, wl.route_scale, wl.swiglu_limit, wl.mode, wl.seed)
+        ffn.layer(sub, wl.top_k, wl.route_scale, wl.swiglu_limit, wl.mode, wl.seed,
+                  weight_format=weight_format)
         dt = time.perf_counter() - t0
         done += n
         t_used += dt
@@ -137,6 +142,11 @@ def main():
                      top_k=wl.top_k, route_scale=wl.route_scale, swiglu_limit=wl.swiglu_limit,
                      route_mode=moe.ROUTE_HASH if wl.mode == "hash" else moe.ROUTE_SQRTSOFTPLUS,
                      hash_seed=wl.seed)
+    fp8 = args.experts == "fp8"
+    if fp8:
+        w = moe.expert_cast_fp8(cfg, w)
+        cfg.expert_format = moe.EXPERTS_FP8
+        torch.cuda.synchronize()
     L = moe.Layer(cfg, w, w_gate=wg, bias=bias, shared=shared)
     y = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device=dev)
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
@@ -192,9 +202,9 @@ def main():
     torch.cuda.synchronize()
     ffn_ms = e0.elapsed_time(e1) / steps
 
-    alg = algorithmic(wl, n_touched)
+    alg = algorithmic(wl, n_touched, fp8)
     src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", "expert_gemm.hip"), "rb").read()
-    traffic = traffic_record(hashlib.sha256(src).hexdigest(), wl.name)
+    traffic = traffic_record(hashlib.sha256(src).hexdigest(), wl.name + ("_fp8" if fp8 else ""))
     ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
     ffn_tflops = alg["flops_routed"] / (ffn_ms * 1e-3) / 1e12
     hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (MFMA_FP8_PEAK_TFLOPS * 1e12)
@@ -204,7 +214,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
-    fam = "expert_gemm_stream" if wl.tokens * wl.top_k <= 32 * wl.n_experts else "expert_gemm_tile"
+    small = wl.tokens * wl.top_k <= 32 * wl.n_experts
+    fam = ("expert_gemm_stream8" if small else "expert_gemm_kernel") if fp8 else \
+          ("expert_gemm_stream" if small else "expert_gemm_tile")
     roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
                       " (+ tile prefix)")
     roof["ms_per_call"] = round(ffn_ms, 4)
@@ -224,7 +236,7 @@ def main():
         del src_buf, dst_buf
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp)
+        cpu = cpu_baseline(wl, inp, weight_format=args.experts)
 
     value = wl.tokens / (ms_step * 1e-3)
     out = {
@@ -238,11 +250,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4e2m1 x fp8e4m3 -> f32 (experts); bf16 -> f32 (router, shared)",
+        "dtype": ("fp8e4m3 x fp8e4m3" if fp8 else "fp4e2m1 x fp8e4m3")
+                 + " -> f32 (experts); bf16 -> f32 (router, shared)",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": f"{wl.name}: T={wl.tokens} H={wl.hidden} I={wl.inter} E={wl.n_experts} "
                                f"top-{wl.top_k} {'hash' if wl.mode == 'hash' else 'sqrtsoftplus'} routing"
-                               f"{' + bf16 shared expert' if wl.shared else ''}",
+                               f"{' + bf16 shared expert' if wl.shared else ''}"
+                               f"{', FP8 experts (per-128 cast of the MXFP4 weights)' if fp8 else ''}",
                    "tokens": wl.tokens, "experts_touched": n_touched,
                    "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2)},
         "layer": {"launch": launch,

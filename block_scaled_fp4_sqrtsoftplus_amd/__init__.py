@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_scaled_fp4_sqrtsoftplus_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python block_scaled_fp4_sqrtsoftplus_amd/build.py` "
         "(hipcc, gfx950); this package has no non-HIP fallback")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -30,6 +30,7 @@ MOE_OK = 0
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL_ARG", "MOE_ERR_BAD_SHAPE", "MOE_ERR_MISALIGNED",
                 "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_UNSUPPORTED", "MOE_ERR_ARCH", "MOE_ERR_HIP"]
 ROUTE_SQRTSOFTPLUS, ROUTE_HASH = 0, 1
+EXPERTS_MXFP4, EXPERTS_FP8 = 0, 1
 OP_ROUTE, OP_EXPERT_FFN, OP_LAYER = 0, 1, 2
 
 
@@ -38,7 +39,8 @@ class MoeConfigC(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
                 ("route_mode", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
-                ("hash_seed", ctypes.c_uint64)]
+                ("hash_seed", ctypes.c_uint64), ("expert_format", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class MoeExpertWeightsC(ctypes.Structure):
@@ -70,6 +72,9 @@ lib.moe_layer.restype = ctypes.c_int
 lib.moe_layer.argtypes = [ctypes.POINTER(MoeConfigC), _vp, _vp, _vp, _vp,
                           ctypes.POINTER(MoeExpertWeightsC), ctypes.POINTER(MoeSharedWeightsC), _vp,
                           ctypes.POINTER(MoeRoutingC), _vp, _sz, _vp]
+lib.moe_expert_cast_fp8.restype = ctypes.c_int
+lib.moe_expert_cast_fp8.argtypes = [ctypes.POINTER(MoeConfigC), ctypes.POINTER(MoeExpertWeightsC),
+                                    ctypes.POINTER(MoeExpertWeightsC), _vp]
 lib.moe_layer_graph_create.restype = ctypes.c_int
 lib.moe_layer_graph_create.argtypes = [ctypes.POINTER(MoeConfigC), _vp, _vp, _vp, _vp,
                                        ctypes.POINTER(MoeExpertWeightsC),
@@ -105,11 +110,12 @@ class Config:
     route_mode: int = ROUTE_SQRTSOFTPLUS
     out_fp32: int = 1
     hash_seed: int = 0
+    expert_format: int = 0          # EXPERTS_MXFP4 or EXPERTS_FP8
 
     def c(self):
         return MoeConfigC(self.tokens, self.hidden, self.inter, self.n_experts, self.top_k,
                           self.route_scale, self.swiglu_limit, self.route_mode, self.out_fp32,
-                          self.hash_seed & ((1 << 64) - 1))
+                          self.hash_seed & ((1 << 64) - 1), self.expert_format, 0)
 
 
 def _ptr(t):
@@ -208,6 +214,22 @@ def expert_ffn(cfg: Config, xq, xs, routing, weights, want_h=False):
     if want_h:
         res.update(hq=hq, hs=hs)
     return res
+
+
+def expert_cast_fp8(cfg: Config, weights):
+    """MXFP4 expert weights -> FP8 expert weights (moe_expert_cast_fp8):
+    returns a dict with w1, w3 [E, I, H], w2 [E, H, I] E4M3 bytes and their
+    per-128 E8M0 scales."""
+    E, H, I = cfg.n_experts, cfg.hidden, cfg.inter
+    dev = weights["w1"].device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {"w1": torch.empty((E, I, H), **u8), "w1_scale": torch.empty((E, I, H // 128), **u8),
+           "w3": torch.empty((E, I, H), **u8), "w3_scale": torch.empty((E, I, H // 128), **u8),
+           "w2": torch.empty((E, H, I), **u8), "w2_scale": torch.empty((E, H, I // 128), **u8)}
+    c = cfg.c()
+    _check(lib.moe_expert_cast_fp8(ctypes.byref(c), ctypes.byref(_weights_c(weights)),
+                                   ctypes.byref(_weights_c(out)), _stream()))
+    return out
 
 
 class Layer:

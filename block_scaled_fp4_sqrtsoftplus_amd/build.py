@@ -1,6 +1,7 @@
 """Build the HIP library libmoe_fp4.so in-tree for gfx950 with hipcc.
 
-Usage: python -m block_scaled_fp4_sqrtsoftplus_amd.build   (or build())
+Usage: python block_scaled_fp4_sqrtsoftplus_amd/build.py   (or __graft_entry__.build()); it
+does not import the package, whose import loads the library.
 Every call recompiles all sources (a few seconds each, in parallel).
 """
 
@@ -14,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_fp4.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "quant_act.hip", "route.hip", "expert_gemm.hip", "bf16_gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quant_act.hip", "route.hip", "expert_gemm.hip", "bf16_gemm.hip", "combine.hip",
+           "cast_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

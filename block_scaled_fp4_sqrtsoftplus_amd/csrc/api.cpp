@@ -35,6 +35,8 @@ moe_status check_cfg(const moe_config* c) {
   if (!(c->swiglu_limit > 0.f)) return MOE_ERR_BAD_SHAPE;  // NaN fails too; +inf allowed
   if (c->route_mode != MOE_ROUTE_SQRTSOFTPLUS && c->route_mode != MOE_ROUTE_HASH)
     return MOE_ERR_BAD_SHAPE;
+  if (c->expert_format != MOE_EXPERTS_MXFP4 && c->expert_format != MOE_EXPERTS_FP8)
+    return MOE_ERR_BAD_SHAPE;
   return MOE_OK;
 }
 
@@ -191,6 +193,7 @@ moe_status check_weights(const moe_expert_weights* w) {
 int choose_bm(const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
   if (P <= (int64_t)32 * c.n_experts) return 16;
+  if (c.expert_format == MOE_EXPERTS_FP8) return 64;     // no 128-pair FP8 tile kernel
   auto tiled = [](int k) { return k == 1024 || k == 2048 || k == 4096; };
   return (tiled(c.hidden) && tiled(c.inter)) ? 128 : 64;
 }
@@ -258,6 +261,7 @@ moe_status enqueue_ffn(const moe_config& c, const uint8_t* xq, const uint8_t* xs
   a.w3_scale = w.w3_scale;
   a.K = c.hidden;
   a.N = c.inter;
+  a.fp8w = c.expert_format == MOE_EXPERTS_FP8;
   a.hq = hq;
   a.hs = hs;
   MOE_TRY(launch_expert_gemm1(a, bm, mt_max, st));
@@ -464,6 +468,24 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
     return s;
   if (shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
   MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, y, c.tokens, c.hidden, c.top_k, st));
+  return MOE_OK;
+}
+
+moe_status moe_expert_cast_fp8(const moe_config* cfg, const moe_expert_weights* src,
+                               const moe_expert_weights* dst, void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(src)) != MOE_OK || (s = check_weights(dst)) != MOE_OK) return s;
+  if ((s = check_device()) != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t E = c.n_experts;
+  MOE_TRY(launch_cast_fp8(src->w1, src->w1_scale, const_cast<uint8_t*>(dst->w1),
+                          const_cast<uint8_t*>(dst->w1_scale), E * c.inter, c.hidden, st));
+  MOE_TRY(launch_cast_fp8(src->w3, src->w3_scale, const_cast<uint8_t*>(dst->w3),
+                          const_cast<uint8_t*>(dst->w3_scale), E * c.inter, c.hidden, st));
+  MOE_TRY(launch_cast_fp8(src->w2, src->w2_scale, const_cast<uint8_t*>(dst->w2),
+                          const_cast<uint8_t*>(dst->w2_scale), E * c.hidden, c.inter, st));
   return MOE_OK;
 }
 

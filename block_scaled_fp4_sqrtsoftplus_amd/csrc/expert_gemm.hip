@@ -74,6 +74,23 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& b0, con
   return acc;
 }
 
+// FP8 weights (E4M3, cbsz 0): A is 32 bytes per lane laid out like the FP8
+// activation operand (bytes 0-15: K = 16*(l/16) + j, bytes 16-31:
+// K = 64 + 16*(l/16) + j); one scale per 128 for all four lane groups.
+__device__ __forceinline__ v4f mfma_fp8_fp8(const uint4& a0, const uint4& a1, const uint4& b0,
+                                            const uint4& b1, v4f acc, int sa, int sb) {
+  v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  asm volatile(
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : "+v"(acc)
+      : "v"(av), "v"(bv), "v"(sa), "v"(sb));
+  return acc;
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // Maps the workgroup to (n_tile, expert, m0); returns false when idle.
@@ -129,7 +146,7 @@ __device__ __forceinline__ bool map_tile_grouped(const ExpertGemmArgs& p, int n_
   return true;
 }
 
-template <int MODE, int MT>
+template <int MODE, int MT, bool FP8W = false>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {
   constexpr int BM = 16 * MT;
@@ -147,8 +164,11 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
   const int grp = lane >> 4;   // K group
   const int K = p.K, N = p.N;
   const int S = K / 128;
-  const size_t wrow_bytes = (size_t)K / 2;
-  const size_t srow_bytes = (size_t)K / 32;
+  // FP4: K/2 bytes per row and a scale per 32 (this lane's K block: + grp);
+  // FP8: K bytes per row and one scale per 128 (per K step)
+  const size_t wrow_bytes = FP8W ? (size_t)K : (size_t)K / 2;
+  const size_t srow_bytes = FP8W ? (size_t)K / 128 : (size_t)K / 32;
+  const int sgrp = FP8W ? 0 : grp;
 
   // ---- weight rows of this wave (4 MFMA row tiles) ----
   const uint8_t* wptr[4];
@@ -163,7 +183,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
       wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + sgrp;
     }
   } else {
     n0 = n_tile * kG2Rows;
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
     for (int t = 0; t < 4; ++t) {
       const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
       wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + sgrp;
     }
   }
 
@@ -208,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
   // stage X holds one K step's weight bytes, scale bytes and (unstaged)
   // activation bytes, all written by loads only.
   struct Stage {
-    uint4 a[4];
+    uint4 a[4][FP8W ? 2 : 1];
     uint32_t sa[4];
     uint4 b[MT][2];
     uint32_t sb[MT];
@@ -219,8 +239,14 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
     if (wave_live) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        x.a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-        x.sa[t] = sptr[t][(size_t)s * 4];
+        if constexpr (FP8W) {
+          x.a[t][0] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 128);
+          x.a[t][1] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 128 + 64);
+          x.sa[t] = sptr[t][s];
+        } else {
+          x.a[t][0] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
+          x.sa[t] = sptr[t][(size_t)s * 4];
+        }
       }
     }
 #pragma unroll
@@ -255,7 +281,12 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          acc[t][m] = mfma_fp4_fp8(x.a[t], x.b[m][0], x.b[m][1], acc[t][m], (int)x.sa[t], (int)x.sb[m]);
+          if constexpr (FP8W)
+            acc[t][m] = mfma_fp8_fp8(x.a[t][0], x.a[t][FP8W ? 1 : 0], x.b[m][0], x.b[m][1],
+                                     acc[t][m], (int)x.sa[t], (int)x.sb[m]);
+          else
+            acc[t][m] = mfma_fp4_fp8(x.a[t][0], x.b[m][0], x.b[m][1], acc[t][m], (int)x.sa[t],
+                                     (int)x.sb[m]);
     }
   };
   // one K step: compute from x (its activations in LDS buffer `buf` when
@@ -490,6 +521,164 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
     }
     four_steps(yes{}, even{}, Q - 2, SB0, SB1);
     four_steps(no{}, odd{}, Q - 1, SB1, SB0);
+  }
+
+  if (MODE == 1) {
+    float h[2][4];
+    const float lim = p.limit;
+    float amax = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
+        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
+        const float hv = silu_f(g) * u;
+        h[tt][v] = hv;
+        amax = fmaxf(amax, fabsf(hv));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (lane < 16) red[wv][lane] = amax;
+    __syncthreads();
+    const float bmax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+    const int ex = pow2_scale_exp(bmax);
+    if (m0 + col < n_e) {
+      const size_t row = (size_t)(off_e + m0 + col);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[tt][v], -ex)) << (8 * v);
+        *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
+      }
+      if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+    }
+  } else {
+    if (!wave_live || m0 + col >= n_e) return;
+    const size_t row = (size_t)(off_e + m0 + col);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
+      if (p.out_fp32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
+            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+      } else {
+        const uint32_t lo = f32_to_bf16(acc[t][0]) | (f32_to_bf16(acc[t][1]) << 16);
+        const uint32_t hi = f32_to_bf16(acc[t][2]) | (f32_to_bf16(acc[t][3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
+            make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming variant for FP8 expert weights (E4M3 rows of K bytes, one E8M0
+// scale per 128) and m-tiles of at most 16 pairs: each K step reads whole
+// 128-byte weight lines (both operand halves back to back); four steps of
+// weight and activation loads stay in flight in a register ring; the weight
+// and activation scales of four steps arrive as one dword per row / token.
+// ---------------------------------------------------------------------------
+template <int MODE, int S>
+__global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream8(ExpertGemmArgs p, int mt_max,
+                                                                     int n_tiles) {
+  __shared__ float red[4][16];
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  constexpr int K = S * 128;                // S in {8, 16, 32}
+  const int N = p.N;
+
+  const uint8_t* wptr[4];
+  const uint8_t* sptr[4];
+  int n0;
+  bool wave_live = true;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const uint8_t* base = (t < 2) ? p.w : p.w3;
+      const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
+      wptr[t] = base + ((size_t)e * N + row) * K + grp * 16;
+      sptr[t] = sbase + ((size_t)e * N + row) * S;
+    }
+  } else {
+    n0 = n_tile * kG2Rows;
+    wave_live = (n0 + 64 * wv) < N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
+      wptr[t] = p.w + ((size_t)e * N + row) * K + grp * 16;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * S;
+    }
+  }
+  const int slot = min(m0 + col, n_e - 1);
+  const int64_t brow = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
+                                   : (int64_t)(off_e + slot);
+  const uint8_t* bptr = p.a + brow * K + 16 * grp;
+  const uint8_t* bsp = p.a_scale + brow * S;
+
+  v4f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (wave_live) {
+    uint4 A[4][4][2], B[4][2];
+    uint32_t SW0[4], SW1[4], SB0, SB1;
+    auto load_step = [&](int s, uint4 (&a)[4][2], uint4 (&b)[2]) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t][0] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 128);
+        a[t][1] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 128 + 64);
+      }
+      b[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
+      b[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
+    };
+    // scales of steps 4q .. 4q+3: byte d of a dword per weight row / token
+    auto load_sc = [&](int q, uint32_t (&sw)[4], uint32_t& sb) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sw[t] = *reinterpret_cast<const uint32_t*>(sptr[t] + 4 * q);
+      sb = *reinterpret_cast<const uint32_t*>(bsp + 4 * q);
+    };
+    auto four_steps = [&](auto loads, int q, const uint32_t (&swc)[4], uint32_t sbc,
+                          uint32_t (&swn)[4], uint32_t& sbn) {
+      constexpr bool LOADS = decltype(loads)::value;
+      if constexpr (LOADS) load_sc(q + 1, swn, sbn);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int sb = (int)(sbc >> (8 * d));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t] = mfma_fp8_fp8(A[d][t][0], A[d][t][1], B[d][0], B[d][1], acc[t],
+                                (int)(swc[t] >> (8 * d)), sb);
+        if constexpr (LOADS) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_step(4 * q + d + 4, A[d], B[d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    load_sc(0, SW0, SB0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      load_step(d, A[d], B[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int Q = S / 4;  // even, >= 2
+    for (int q = 0; q < Q - 2; q += 2) {
+      four_steps(yes{}, q, SW0, SB0, SW1, SB1);
+      four_steps(yes{}, q + 1, SW1, SB1, SW0, SB0);
+    }
+    four_steps(yes{}, Q - 2, SW0, SB0, SW1, SB1);
+    four_steps(no{}, Q - 1, SW1, SB1, SW0, SB0);
   }
 
   if (MODE == 1) {
@@ -963,6 +1152,26 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
+  if (a.fp8w) {
+    if (bm == 16 && a.K == 4096)
+      hipLaunchKernelGGL((expert_gemm_stream8<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+    else if (bm == 16 && a.K == 2048)
+      hipLaunchKernelGGL((expert_gemm_stream8<MODE, 16>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+    else if (bm == 16 && a.K == 1024)
+      hipLaunchKernelGGL((expert_gemm_stream8<MODE, 8>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                         mt_max, n_tiles);
+    else if (bm == 16)
+      hipLaunchKernelGGL((expert_gemm_kernel<MODE, 1, true>), dim3(grid), dim3(kGemmThreads), 0, st,
+                         a, mt_max, n_tiles);
+    else if (bm == 64)
+      hipLaunchKernelGGL((expert_gemm_kernel<MODE, 4, true>), dim3(grid), dim3(kGemmThreads), 0, st,
+                         a, mt_max, n_tiles);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (bm == 128) {
     if (a.K != 1024 && a.K != 2048 && a.K != 4096) return hipErrorInvalidValue;
     if (a.K == 4096)

@@ -121,11 +121,16 @@ struct ExpertGemmArgs {
   uint8_t* hs;
   void* out;                 // GEMM2 out
   int out_fp32;
+  int fp8w;                  // weights: 0 MXFP4 ([N, K/2] + [N, K/32]), 1 FP8 ([N, K] + [N, K/128])
 };
 
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
 hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+
+// MXFP4 [rows, K/2] + [rows, K/32] -> FP8 E4M3 [rows, K] + E8M0 [rows, K/128].
+hipError_t launch_cast_fp8(const uint8_t* w, const uint8_t* ws, uint8_t* q, uint8_t* qs,
+                           int64_t rows, int K, hipStream_t st);
 
 // Shared expert (bf16): h = bf16(clamped_swiglu(x w1^T, x w3^T)) [T, I];
 // ysh = h w2^T [T, H] fp32.

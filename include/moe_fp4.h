@@ -86,6 +86,13 @@ typedef enum moe_route_mode {
   MOE_ROUTE_HASH = 1          /* SplitMix64 over the token id -> k experts  */
 } moe_route_mode;
 
+/* Routed expert weight format ("DeepSeek-V4-Pro-0813-nvfp4-DSpark" article,
+ * 阶段一: the MXFP4 checkpoint, or its lossless per-128 cast to FP8 experts). */
+typedef enum moe_expert_format {
+  MOE_EXPERTS_MXFP4 = 0,      /* E2M1 nibbles + E8M0 per 32 (the checkpoint) */
+  MOE_EXPERTS_FP8 = 1         /* E4M3 bytes + E8M0 per 128                   */
+} moe_expert_format;
+
 typedef enum moe_op {
   MOE_OP_ROUTE = 0,
   MOE_OP_EXPERT_FFN = 1,
@@ -108,13 +115,18 @@ typedef struct moe_config {
   int32_t route_mode;  /* moe_route_mode                                   */
   int32_t out_fp32;    /* moe_expert_ffn: 1 -> out_pairs fp32, 0 -> bf16   */
   uint64_t hash_seed;  /* MOE_ROUTE_HASH only                              */
+  int32_t expert_format; /* moe_expert_format of the routed expert weights  */
+  int32_t reserved;      /* set to 0                                       */
 } moe_config;
 
 /* Routed expert weights, stacked over experts, checkpoint layout:
  *   w1, w3:             [E, I, H/2] bytes, E2M1 nibbles along H (K)
  *   w1_scale, w3_scale: [E, I, H/32] E8M0 bytes
  *   w2:                 [E, H, I/2] bytes, E2M1 nibbles along I (K)
- *   w2_scale:           [E, H, I/32] E8M0 bytes                        */
+ *   w2_scale:           [E, H, I/32] E8M0 bytes
+ * With expert_format MOE_EXPERTS_FP8: w1, w3 [E, I, H] and w2 [E, H, I]
+ * E4M3 bytes, scales [E, I, H/128] and [E, H, I/128] E8M0 bytes
+ * (moe_expert_cast_fp8 writes them).                                   */
 typedef struct moe_expert_weights {
   const uint8_t* w1;
   const uint8_t* w1_scale;
@@ -200,6 +212,17 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
                      const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
                      const moe_shared_weights* shared, uint16_t* y,
                      const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP4 -> FP8 expert weights ("DeepSeek-V4-Pro-0813-nvfp4-DSpark" article,
+ * 阶段一, 关于 MXFP4 的无损种子): per row and 128 elements of K the new E8M0
+ * exponent is the largest of the four per-32 exponents, and each element is
+ * the E4M3 code (round to nearest even, sign kept) of its E2M1 value times
+ * 2^(its exponent - the new one).  Lossless when the four exponents of every
+ * block span at most 8.  src: MXFP4 layout, dst: FP8 layout (see
+ * moe_expert_weights), both for cfg's E, H, I (cfg->expert_format ignored);
+ * caller-owned device buffers, 16-byte aligned, not overlapping. */
+moe_status moe_expert_cast_fp8(const moe_config* cfg, const moe_expert_weights* src,
+                               const moe_expert_weights* dst, void* stream);
 
 /* Graph replay of the layer ("DeepSeek-V4-Flash-SI" card, 模型推理 /
  * 推理模式: the MoE GEMM path captured into a graph to cut kernel-launch

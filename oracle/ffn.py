@@ -41,12 +41,13 @@ def clamped_swiglu(g, u, limit):
     return silu(gc) * uc
 
 
-def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None):
+def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_format="mxfp4"):
     """Routed experts on quantized activations.
 
     xq u8 [T, H], xs u8 [T, H/128]; routing from route.route; w dict with
     w1, w1_scale, w3, w3_scale ([E, I, H/2], [E, I, H/32]) and w2, w2_scale
-    ([E, H, I/2], [E, H, I/32]).
+    ([E, H, I/2], [E, H, I/32]); with weight_format "fp8" the FP8 expert
+    layout instead: [E, N, K] E4M3 bytes with [E, N, K/128] scales.
     Returns dict: hq u8 [P, I], hs u8 [P, I/128], h fp32 [P, I] (before its
     quantization) and o float64 [P, H], all rows in sorted-pair order.
     """
@@ -56,6 +57,7 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None):
     E = off.size - 1
     I = w["w1"].shape[1]
     H = w["w2"].shape[1]
+    deq = quant.fp8_dequant if weight_format == "fp8" else quant.mxfp4_dequant
     hq = np.zeros((P, I), np.uint8)
     hs = np.zeros((P, I // 128), np.uint8)
     hf = np.zeros((P, I), np.float32)
@@ -66,9 +68,9 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None):
             continue
         tok = sp[lo:hi] // top_k
         xd = quant.act_dequant(xq[tok], xs[tok])
-        W1 = quant.mxfp4_dequant(w["w1"][e], w["w1_scale"][e])
-        W3 = quant.mxfp4_dequant(w["w3"][e], w["w3_scale"][e])
-        W2 = quant.mxfp4_dequant(w["w2"][e], w["w2_scale"][e])
+        W1 = deq(w["w1"][e], w["w1_scale"][e])
+        W3 = deq(w["w3"][e], w["w3_scale"][e])
+        W2 = deq(w["w2"][e], w["w2_scale"][e])
         g = xd @ W1.T
         u = xd @ W3.T
         h = clamped_swiglu(g, u, limit).astype(np.float32)
@@ -100,8 +102,11 @@ def combine(o, routing, ysh=None):
     return y
 
 
-def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0):
-    """The whole MoE FFN layer on the inputs of synth.make_inputs.
+def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0,
+          weight_format="mxfp4"):
+    """The whole MoE FFN layer on the inputs of synth.make_inputs; with
+    weight_format "fp8" the routed experts run on the FP8 cast of the MXFP4
+    weights (quant.fp8_experts_from_mxfp4).
 
     Returns dict with the routing, xq/xs, hq/hs, o, ysh (or None), y (float64)
     and y_bf16 (uint16 bit patterns)."""
@@ -114,7 +119,8 @@ def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0):
     else:
         r = route_mod.route(x, inp["w_gate"], k=top_k, bias=inp.get("bias"),
                             route_scale=route_scale)
-    f = expert_ffn(xq, xs, r, inp, top_k, limit)
+    w = quant.fp8_experts_from_mxfp4(inp) if weight_format == "fp8" else inp
+    f = expert_ffn(xq, xs, r, w, top_k, limit, weight_format=weight_format)
     ysh = None
     if inp.get("shared_w1") is not None:
         ysh = shared_expert(x, inp["shared_w1"], inp["shared_w3"], inp["shared_w2"], limit)

@@ -13,7 +13,10 @@
                    block as NVFP4 (same nibbles, one E4M3 scale per 16
                    elements): "DeepSeek-V4-Pro-0813-nvfp4-DSpark", 阶段三导出.
 * e4m3_from_mxfp4 - the lossless E2M1 -> E4M3 cast with the scale rewritten
-                   per 128-block: same article, "关于 MXFP4 的无损种子".
+                   per 128-block: same article, 阶段一 ("关于 MXFP4 的无损种子"),
+                   which also names the FP8-expert checkpoint option.
+* fp8_dequant    - FP8 expert weights as that cast leaves them: E4M3 bytes
+                   [N, K] with one E8M0 scale per 128 elements of K.
 
 Readings where the pages are silent (listed with the others in the design
 notes):
@@ -126,3 +129,23 @@ def e4m3_from_mxfp4(packed, scales):
     rel = np.repeat(e32 - np.repeat(e128, 4, axis=1), 32, axis=1)  # [n, k], <= 0
     vals = formats.e2m1_decode(codes) * np.ldexp(1.0, rel)
     return formats.e4m3_encode(vals), (e128 + 127).astype(np.uint8)
+
+
+def fp8_dequant(codes, scales, block=ACT_BLOCK):
+    """Dequantize one [N, K] FP8 expert matrix (E4M3 bytes, one E8M0 scale
+    per 128 elements of K) to float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    assert scales.shape == (n, k // block)
+    val = formats.e4m3_decode(codes).astype(np.float64).reshape(n, k // block, block)
+    return (val * formats.e8m0_decode(scales)[:, :, None]).reshape(n, k)
+
+
+def fp8_experts_from_mxfp4(w):
+    """All routed expert matrices of a weight dict (w1, w3, w2 and their
+    scales, stacked over experts) cast to FP8 with e4m3_from_mxfp4."""
+    out = {}
+    for n in ("w1", "w3", "w2"):
+        q, sc = zip(*(e4m3_from_mxfp4(w[n][e], w[n + "_scale"][e]) for e in range(w[n].shape[0])))
+        out[n], out[n + "_scale"] = np.stack(q), np.stack(sc)
+    return out

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_quant_act", "moe_route",
                           "moe_expert_ffn", "moe_layer", "moe_layer_graph_create",
-                          "moe_graph_launch", "moe_graph_destroy"}
+                          "moe_graph_launch", "moe_graph_destroy", "moe_expert_cast_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -125,6 +125,20 @@ def test_graph_argument_errors():
                                       16, None, 16, need - 1, ctypes.byref(h)) == 4
     assert lib.moe_graph_launch(None, None) == 1
     assert lib.moe_graph_destroy(None) == 0
+
+
+def test_expert_format_and_cast_argument_errors():
+    c = _cfg()
+    c.expert_format = 2
+    assert lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER) == 0
+    assert lib.moe_layer(ctypes.byref(c), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
+                         1 << 40, None) == 2
+    c.expert_format = 1
+    assert lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER) > 0
+    # cast: NULL / misaligned source or destination arrays
+    assert lib.moe_expert_cast_fp8(ctypes.byref(c), None, ctypes.byref(_w()), None) == 1
+    assert lib.moe_expert_cast_fp8(ctypes.byref(c), ctypes.byref(_w()), ctypes.byref(_w(w2=None)), None) == 1
+    assert lib.moe_expert_cast_fp8(ctypes.byref(c), ctypes.byref(_w(w1_scale=20)), ctypes.byref(_w()), None) == 3
 
 
 def test_quant_act_argument_errors():

@@ -1,0 +1,93 @@
+"""FP8 expert weights: the GPU MXFP4 -> FP8 cast (moe_expert_cast_fp8)
+against the oracle's e4m3_from_mxfp4, bit for bit, and the routed experts /
+whole layer with expert_format = FP8 against the oracle on the cast weights
+("DeepSeek-V4-Pro-0813-nvfp4-DSpark" article, 阶段一: the lossless per-128
+cast and the FP8-expert checkpoint option)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import config, dev, device_inputs, host, norm_err
+from oracle import ffn, formats, quant
+from test_gpu_kernels import _bounds, _check_hq, _check_o, _ffn_case
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("block_scaled_fp4_sqrtsoftplus_amd")
+
+TOL = 2e-2
+
+
+def _gpu_cast(cfg, inp):
+    w = {n: dev(inp[n]) for n in ("w1", "w1_scale", "w3", "w3_scale", "w2", "w2_scale")}
+    f8 = moe.expert_cast_fp8(cfg, w)
+    torch.cuda.synchronize()
+    return f8
+
+
+@pytest.mark.parametrize("spread", [2, 12])
+def test_cast_bit_exact(spread):
+    wl = synth.WORKLOADS["tiny"].replace(hidden=1024, inter=512, n_experts=4, top_k=2)
+    inp = synth.make_inputs(wl, tokens=4)
+    if spread > 2:
+        # exponents spanning up to `spread` within a 128-block: the smallest
+        # values of a block lose bits (rounded to nearest even, or to zero)
+        rng = np.random.default_rng(77)
+        for n in ("w1_scale", "w3_scale", "w2_scale"):
+            inp[n] = rng.integers(127 - spread, 128, inp[n].shape).astype(np.uint8)
+    cfg = config(moe, wl, tokens=4)
+    got = _gpu_cast(cfg, inp)
+    want = quant.fp8_experts_from_mxfp4(inp)
+    for n in want:
+        assert np.array_equal(host(got[n]), want[n]), n
+    if spread > 8:       # the test really exercised lossy blocks
+        e = 0
+        assert not np.array_equal(quant.fp8_dequant(want["w1"][e], want["w1_scale"][e]),
+                                  quant.mxfp4_dequant(inp["w1"][e], inp["w1_scale"][e]))
+
+
+@pytest.mark.parametrize("shape", [
+    ("decode", 8, dict(n_experts=16)),                                 # streaming, K = 4096 / 2048
+    ("decode", 10, dict(hidden=1024, inter=1024, n_experts=8)),        # streaming, K = 1024
+    ("tiny", 37, dict(hidden=512, inter=384, n_experts=12, top_k=3)),  # 16-pair tiles, other K
+    ("tiny", 200, dict(hidden=256, inter=256, n_experts=8, top_k=2)),  # 64-pair tiles
+    ("decode", 400, dict(n_experts=8, top_k=2)),                       # 64-pair tiles, full K
+])
+def test_fp8_expert_ffn_parity(shape):
+    name, tokens, over = shape
+    wl = synth.WORKLOADS[name].replace(**over)
+    inp, xq, xs, r, ref = _ffn_case(wl, tokens)
+    # synthetic exponents span 3 values: the cast is lossless and the oracle's
+    # FP8 expert FFN equals its MXFP4 one (a CPU test pins that)
+    T = inp["x"].shape[0]
+    cfg = config(moe, wl, tokens=T, expert_format=moe.EXPERTS_FP8)
+    w8 = _gpu_cast(config(moe, wl, tokens=T), inp)
+    routing = {n: dev(r[n]) for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_pos")}
+    g = moe.expert_ffn(cfg, dev(xq), dev(xs), routing, w8, want_h=True)
+    torch.cuda.synchronize()
+    dh, absw2 = _bounds(inp, xq, xs, r, ref, wl)
+    hq, hs = host(g["hq"]), host(g["hs"])
+    _check_hq(hq, hs, ref, dh, max_flip_frac=0.02)
+    _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
+
+
+@pytest.mark.parametrize("shape", [
+    ("tiny", 45, dict(hidden=512, inter=384, n_experts=12, top_k=3, shared=True)),
+    ("decode", 5, dict(n_experts=12)),
+])
+def test_fp8_layer_parity(shape):
+    name, tokens, over = shape
+    wl = synth.WORKLOADS[name].replace(**over)
+    inp = synth.make_inputs(wl, tokens=tokens)
+    d = device_inputs(inp)
+    T = inp["x"].shape[0]
+    w8 = moe.expert_cast_fp8(config(moe, wl, tokens=T), d["weights"])
+    cfg = config(moe, wl, tokens=T, expert_format=moe.EXPERTS_FP8)
+    y = moe.layer(cfg, d["x"], w8, w_gate=d["w_gate"], bias=d["bias"], shared=d["shared"])
+    torch.cuda.synchronize()
+    ref = ffn.layer(inp, wl.top_k, wl.route_scale, wl.swiglu_limit, weight_format="fp8")
+    err = norm_err(formats.bf16_decode(host(y)), ref["y"])
+    print(f"fp8 experts {name}{over}: layer error {err:.2e}")
+    assert err <= TOL

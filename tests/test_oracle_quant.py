@@ -10,7 +10,8 @@ import os
 import numpy as np
 import torch
 
-from oracle import formats, quant
+import synth
+from oracle import ffn, formats, quant, route
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -159,6 +160,37 @@ def test_e2m1_to_e4m3_per128_cast():
     v2 = torch.tensor(q2).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     d2 = (v2.reshape(n, k // 128, 128) * np.ldexp(1.0, s2.astype(np.int64) - 127)[:, :, None]).reshape(n, k)
     assert not np.array_equal(d2, quant.mxfp4_dequant(packed2, scales2))
+
+
+def test_fp8_dequant_vs_library_route():
+    rng = np.random.default_rng(16)
+    n, k = 8, 512
+    codes = rng.integers(0, 256, (n, k), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                            # no NaN codes
+    scales = rng.integers(110, 140, (n, k // 128), dtype=np.uint8)
+    vals = torch.tensor(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = vals * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 128, axis=1)
+    assert np.array_equal(quant.fp8_dequant(codes, scales), want)
+
+
+def test_fp8_experts_equal_mxfp4_experts_when_lossless():
+    # the synthetic exponents span 3 values: the cast is lossless, so the FP8
+    # expert path must give bit-identical h bytes and outputs
+    wl = synth.WORKLOADS["tiny"].replace(hidden=512, inter=256, n_experts=6, top_k=2)
+    inp = synth.make_inputs(wl, tokens=24)
+    f8 = quant.fp8_experts_from_mxfp4(inp)
+    assert f8["w1"].shape == (6, 256, 512) and f8["w1_scale"].shape == (6, 256, 4)
+    assert f8["w2"].shape == (6, 512, 256) and f8["w2_scale"].shape == (6, 512, 2)
+    for e in range(6):
+        for nme in ("w1", "w3", "w2"):
+            assert np.array_equal(quant.fp8_dequant(f8[nme][e], f8[nme + "_scale"][e]),
+                                  quant.mxfp4_dequant(inp[nme][e], inp[nme + "_scale"][e]))
+    xq, xs = quant.act_quant(formats.bf16_decode(inp["x"]))
+    r = route.route(inp["x"], inp["w_gate"], k=2)
+    a = ffn.expert_ffn(xq, xs, r, inp, 2)
+    b = ffn.expert_ffn(xq, xs, r, f8, 2, weight_format="fp8")
+    for key in ("hq", "hs", "h", "o"):
+        assert np.array_equal(a[key], b[key]), key
 
 
 def test_expert_layout_matches_printed_shapes():
