@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # dense FP8 (an FP4 x FP8 scaled MFMA issues at most at this rate)
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 EXPERT_BYTES = None              # set from the workload
 
 
@@ -35,21 +36,24 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="report graph replays of the layer (moe_graph_launch) as the step; "
                          "both are timed and reported either way")
-    ap.add_argument("--experts", choices=("mxfp4", "fp8"), default="mxfp4",
-                    help="routed expert weights: the MXFP4 checkpoint format, or its "
-                         "per-128 cast to FP8 (made on the GPU before timing)")
+    ap.add_argument("--experts", choices=("mxfp4", "fp8", "nvfp4"), default="mxfp4",
+                    help="routed expert weights: the MXFP4 checkpoint format, its per-128 "
+                         "cast to FP8 (made on the GPU before timing), or NVFP4 (the same "
+                         "nibbles with synthetic per-16 E4M3 scales)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
-def algorithmic(wl, n_touched, fp8=False):
+def algorithmic(wl, n_touched, fmt="mxfp4"):
     """Bytes and flops the layer must move / compute (no padding, no
     intermediates): weights of the touched experts (FP4 nibbles + E8M0
-    scales per 32 of w1, w3, w2; FP8 experts: E4M3 bytes + E8M0 per 128),
+    scales per 32 of w1, w3, w2; FP8 experts: E4M3 bytes + E8M0 per 128;
+    NVFP4: nibbles + E4M3 per 16),
     the bf16 shared expert and gate, x in, y out."""
     T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.n_experts, wl.top_k
-    per_expert = 3 * (I * H + I * H // 128) if fp8 else 3 * (I * H // 2 + I * H // 32)
+    per_expert = {"mxfp4": 3 * (I * H // 2 + I * H // 32), "fp8": 3 * (I * H + I * H // 128),
+                  "nvfp4": 3 * (I * H // 2 + I * H // 16)}[fmt]
     ffn_bytes = n_touched * per_expert + T * (H + H // 128) + T * k * H * 4
     shared = 3 * I * H * 2 if wl.shared else 0
     gate = E * H * 2 if wl.mode != "hash" else 0
@@ -147,6 +151,11 @@ def main():
         w = moe.expert_cast_fp8(cfg, w)
         cfg.expert_format = moe.EXPERTS_FP8
         torch.cuda.synchronize()
+    if args.experts == "nvfp4":
+        inp.update(synth.nvfp4_scales(wl))
+        for n in ("w1_scale", "w3_scale", "w2_scale"):
+            w[n] = d(inp[n])
+        cfg.expert_format = moe.EXPERTS_NVFP4
     L = moe.Layer(cfg, w, w_gate=wg, bias=bias, shared=shared)
     y = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device=dev)
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
@@ -202,21 +211,25 @@ def main():
     torch.cuda.synchronize()
     ffn_ms = e0.elapsed_time(e1) / steps
 
-    alg = algorithmic(wl, n_touched, fp8)
+    alg = algorithmic(wl, n_touched, args.experts)
     src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", "expert_gemm.hip"), "rb").read()
-    traffic = traffic_record(hashlib.sha256(src).hexdigest(), wl.name + ("_fp8" if fp8 else ""))
+    traffic = traffic_record(hashlib.sha256(src).hexdigest(),
+                             wl.name + ("" if args.experts == "mxfp4" else "_" + args.experts))
     ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
     ffn_tflops = alg["flops_routed"] / (ffn_ms * 1e-3) / 1e12
-    hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+    # the NVFP4 path dequantizes to fp16 and runs on the fp16 MFMA (the bf16 / fp16 peak)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if args.experts == "nvfp4" else MFMA_FP8_PEAK_TFLOPS
+    hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (mfma_peak * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(ffn_tflops / mfma_peak, 4), "traffic": traffic}
     small = wl.tokens * wl.top_k <= 32 * wl.n_experts
-    fam = ("expert_gemm_stream8" if small else "expert_gemm_kernel") if fp8 else \
-          ("expert_gemm_stream" if small else "expert_gemm_tile")
+    fam = {"fp8": "expert_gemm_stream8" if small else "expert_gemm_kernel",
+           "nvfp4": "expert_gemm_nv",
+           "mxfp4": "expert_gemm_stream" if small else "expert_gemm_tile"}[args.experts]
     roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
                       " (+ tile prefix)")
     roof["ms_per_call"] = round(ffn_ms, 4)
@@ -224,7 +237,7 @@ def main():
     roof["alg_flops_per_call"] = alg["flops_routed"]
 
     layer_t_roof = max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
-                       alg["flops_routed"] / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+                       alg["flops_routed"] / (mfma_peak * 1e12)
                        + alg["flops_shared"] / 2.5e15 + alg["flops_router"] / 2.5e15)
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
@@ -236,7 +249,7 @@ def main():
         del src_buf, dst_buf
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, weight_format=args.experts)
+        cpu = cpu_baseline(wl, inp, weight_format=args.experts)   # inp holds the NVFP4 scales then
 
     value = wl.tokens / (ms_step * 1e-3)
     out = {
@@ -250,13 +263,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8e4m3 x fp8e4m3" if fp8 else "fp4e2m1 x fp8e4m3")
-                 + " -> f32 (experts); bf16 -> f32 (router, shared)",
+        "dtype": {"fp8": "fp8e4m3 x fp8e4m3 -> f32", "mxfp4": "fp4e2m1 x fp8e4m3 -> f32",
+                  "nvfp4": "fp16(fp4e2m1 x e4m3 scale) x fp16(fp8e4m3) -> f32"}[args.experts]
+                 + " (experts); bf16 -> f32 (router, shared)",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": f"{wl.name}: T={wl.tokens} H={wl.hidden} I={wl.inter} E={wl.n_experts} "
                                f"top-{wl.top_k} {'hash' if wl.mode == 'hash' else 'sqrtsoftplus'} routing"
                                f"{' + bf16 shared expert' if wl.shared else ''}"
-                               f"{', FP8 experts (per-128 cast of the MXFP4 weights)' if fp8 else ''}",
+                               f"{', FP8 experts (per-128 cast of the MXFP4 weights)' if fp8 else ''}"
+                               f"{', NVFP4 experts (per-16 E4M3 scales)' if args.experts == 'nvfp4' else ''}",
                    "tokens": wl.tokens, "experts_touched": n_touched,
                    "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2)},
         "layer": {"launch": launch,

@@ -127,6 +127,9 @@ struct ExpertGemmArgs {
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
 hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+// NVFP4 weights (E4M3 scale per 16), m-tiles of 16 pairs, K % 512 == 0.
+hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
+hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
 
 // MXFP4 [rows, K/2] + [rows, K/32] -> FP8 E4M3 [rows, K] + E8M0 [rows, K/128].
 hipError_t launch_cast_fp8(const uint8_t* w, const uint8_t* ws, uint8_t* q, uint8_t* qs,

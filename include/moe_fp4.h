@@ -90,7 +90,10 @@ typedef enum moe_route_mode {
  * 阶段一: the MXFP4 checkpoint, or its lossless per-128 cast to FP8 experts). */
 typedef enum moe_expert_format {
   MOE_EXPERTS_MXFP4 = 0,      /* E2M1 nibbles + E8M0 per 32 (the checkpoint) */
-  MOE_EXPERTS_FP8 = 1         /* E4M3 bytes + E8M0 per 128                   */
+  MOE_EXPERTS_FP8 = 1,        /* E4M3 bytes + E8M0 per 128                   */
+  MOE_EXPERTS_NVFP4 = 2       /* E2M1 nibbles + E4M3 per 16 (阶段三导出);
+                                 needs hidden % 512 == 0 and inter % 512 == 0,
+                                 else MOE_ERR_UNSUPPORTED                   */
 } moe_expert_format;
 
 typedef enum moe_op {
@@ -126,7 +129,9 @@ typedef struct moe_config {
  *   w2_scale:           [E, H, I/32] E8M0 bytes
  * With expert_format MOE_EXPERTS_FP8: w1, w3 [E, I, H] and w2 [E, H, I]
  * E4M3 bytes, scales [E, I, H/128] and [E, H, I/128] E8M0 bytes
- * (moe_expert_cast_fp8 writes them).                                   */
+ * (moe_expert_cast_fp8 writes them).  With MOE_EXPERTS_NVFP4: the nibble
+ * arrays as for MXFP4, scales [E, I, H/16] and [E, H, I/16] E4M3 bytes
+ * (one per 16 elements of K, no per-tensor scale).                     */
 typedef struct moe_expert_weights {
   const uint8_t* w1;
   const uint8_t* w1_scale;

@@ -132,3 +132,22 @@ def make_inputs(wl: Workload, tokens=None, experts_only=None):
         out["shared_w1"] = out["shared_w3"] = out["shared_w2"] = None
     out["token_ids"] = rng(6).integers(0, VOCAB, size=T, dtype=np.int64)
     return out
+
+
+def nvfp4_scales(wl: Workload, experts_only=None):
+    """Per-16 E4M3 scale bytes for NVFP4 expert weights of workload `wl`
+    (the nibble arrays of make_inputs are reused): positive E4M3 codes with
+    exponent field 1 and a uniform mantissa, i.e. values (1 + m/8) * 2**-6,
+    so every scale carries mantissa bits.  Returns w1_scale, w3_scale
+    [E, I, H/16] and w2_scale [E, H, I/16] uint8."""
+    H, I, E = wl.hidden, wl.inter, wl.n_experts
+    keep = None if experts_only is None else set(int(e) for e in experts_only)
+    out = {"w1_scale": np.zeros((E, I, H // 16), np.uint8), "w3_scale": np.zeros((E, I, H // 16), np.uint8),
+           "w2_scale": np.zeros((E, H, I // 16), np.uint8)}
+    for e in range(E):
+        if keep is not None and e not in keep:
+            continue
+        r = np.random.Generator(np.random.PCG64([wl.seed, 7, e]))
+        for n, shape in (("w1_scale", (I, H // 16)), ("w3_scale", (I, H // 16)), ("w2_scale", (H, I // 16))):
+            out[n][e] = (0x08 | r.integers(0, 8, size=shape)).astype(np.uint8)
+    return out

@@ -129,12 +129,19 @@ def test_graph_argument_errors():
 
 def test_expert_format_and_cast_argument_errors():
     c = _cfg()
-    c.expert_format = 2
+    c.expert_format = 3
     assert lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER) == 0
     assert lib.moe_layer(ctypes.byref(c), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
                          1 << 40, None) == 2
     c.expert_format = 1
     assert lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER) > 0
+    # NVFP4 experts need K % 512 == 0 for both GEMMs
+    n = _cfg(hidden=4096, inter=384)
+    n.expert_format = 2
+    assert lib.moe_layer(ctypes.byref(n), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
+                         1 << 40, None) == 5
+    n.inter = 512
+    assert lib.moe_workspace_size(ctypes.byref(n), moe.OP_LAYER) > 0
     # cast: NULL / misaligned source or destination arrays
     assert lib.moe_expert_cast_fp8(ctypes.byref(c), None, ctypes.byref(_w()), None) == 1
     assert lib.moe_expert_cast_fp8(ctypes.byref(c), ctypes.byref(_w()), ctypes.byref(_w(w2=None)), None) == 1

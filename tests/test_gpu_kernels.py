@@ -151,9 +151,11 @@ def _ffn_case(wl, tokens, seed_tokens=None):
 TAU = 2.0 ** -13
 
 
-def _bounds(inp, xq, xs, r, ref, wl):
+def _bounds(inp, xq, xs, r, ref, wl, deq=quant.mxfp4_dequant, tau=None):
     """Per element of h and o: how far the GPU may sit from the oracle given
-    TAU accumulation error in each GEMM (and h's fp32 rounding)."""
+    tau (default TAU) accumulation error in each GEMM (and h's fp32
+    rounding); deq dequantizes the expert weights."""
+    tau = TAU if tau is None else tau
     off, sp = r["expert_offsets"], r["sorted_pairs"]
     P, I = ref["hq"].shape
     dh = np.zeros((P, I))
@@ -165,14 +167,14 @@ def _bounds(inp, xq, xs, r, ref, wl):
             continue
         tok = sp[lo:hi] // wl.top_k
         xd = quant.act_dequant(xq[tok], xs[tok])
-        W1 = quant.mxfp4_dequant(inp["w1"][e], inp["w1_scale"][e])
-        W3 = quant.mxfp4_dequant(inp["w3"][e], inp["w3_scale"][e])
+        W1 = deq(inp["w1"][e], inp["w1_scale"][e])
+        W3 = deq(inp["w3"][e], inp["w3_scale"][e])
         g, u = xd @ W1.T, xd @ W3.T
-        bg, bu = TAU * (np.abs(xd) @ np.abs(W1).T), TAU * (np.abs(xd) @ np.abs(W3).T)
+        bg, bu = tau * (np.abs(xd) @ np.abs(W1).T), tau * (np.abs(xd) @ np.abs(W3).T)
         gc, uc = np.clip(g, -lim, lim), np.clip(u, -lim, lim)
         dsilu = 1.1                                   # |d silu / dg| <= 1.0999
         dh[lo:hi] = dsilu * np.abs(uc) * bg + np.abs(ffn.silu(gc)) * bu + 2.0 ** -23 * np.abs(ffn.silu(gc) * uc)
-        absw2[e] = np.abs(quant.mxfp4_dequant(inp["w2"][e], inp["w2_scale"][e]))
+        absw2[e] = np.abs(deq(inp["w2"][e], inp["w2_scale"][e]))
     return dh, absw2
 
 
@@ -207,16 +209,17 @@ def _check_hq(hq, hs, ref, dh, max_flip_frac):
     return diff
 
 
-def _check_o(o, hq, hs, ref, r, absw2):
+def _check_o(o, hq, hs, ref, r, absw2, tau=None):
     """o = deq(hq) w2^T: the GPU may differ from the oracle by its own codes'
     difference propagated through |w2| plus TAU accumulation error."""
+    tau = TAU if tau is None else tau
     off = r["expert_offsets"]
     dq = quant.act_dequant(hq, hs)
     dr = quant.act_dequant(ref["hq"], ref["hs"])
     bound = np.zeros_like(o)
     for e, aw in absw2.items():
         lo, hi = int(off[e]), int(off[e + 1])
-        bound[lo:hi] = np.abs(dq[lo:hi] - dr[lo:hi]) @ aw.T + TAU * (np.abs(dq[lo:hi]) @ aw.T)
+        bound[lo:hi] = np.abs(dq[lo:hi] - dr[lo:hi]) @ aw.T + tau * (np.abs(dq[lo:hi]) @ aw.T)
     bad = np.abs(o - ref["o"]) > bound + 1e-30
     assert not bad.any(), f"{bad.sum()} outputs outside the bound"
     print(f"o: normalised max error {norm_err(o, ref['o']):.2e}")

@@ -119,6 +119,38 @@ def test_mxfp4_dequant_vs_library_route():
     assert np.array_equal(ours, ref)
 
 
+def test_nvfp4_dequant_vs_library_route():
+    # per-16 E4M3 scales with mantissa bits, decoded through torch's fp8 type
+    rng = np.random.default_rng(17)
+    n, k = 24, 256
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    s16 = (rng.integers(1, 15, (n, k // 16)) << 3 | rng.integers(0, 8, (n, k // 16))).astype(np.uint8)
+    ours = quant.nvfp4_dequant(packed, s16)
+    lo, hi = packed & 0xF, packed >> 4
+    codes = np.stack([lo, hi], axis=2).reshape(n, k)
+    vals = torch.tensor(_e2m1_as_e4m3_byte(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    sc = torch.tensor(s16).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = (vals.reshape(n, k // 16, 16) * sc[:, :, None]).reshape(n, k).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_nvfp4_experts_equal_mxfp4_experts_when_lossless():
+    # MXFP4 re-expressed as NVFP4 (power-of-two per-16 scales): the oracle's
+    # NVFP4 expert FFN must reproduce the MXFP4 one bit for bit
+    wl = synth.WORKLOADS["tiny"].replace(hidden=512, inter=256, n_experts=5, top_k=2)
+    inp = synth.make_inputs(wl, tokens=20)
+    nv = {}
+    for nme in ("w1", "w3", "w2"):
+        q, sc = zip(*(quant.nvfp4_from_mxfp4(inp[nme][e], inp[nme + "_scale"][e]) for e in range(5)))
+        nv[nme], nv[nme + "_scale"] = np.stack(q), np.stack(sc)
+    xq, xs = quant.act_quant(formats.bf16_decode(inp["x"]))
+    r = route.route(inp["x"], inp["w_gate"], k=2)
+    a = ffn.expert_ffn(xq, xs, r, inp, 2)
+    b = ffn.expert_ffn(xq, xs, r, nv, 2, weight_format="nvfp4")
+    for key in ("hq", "hs", "h", "o"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_mxfp4_to_nvfp4_lossless():
     # same nibbles, per-16 E4M3 scales: identical values whenever 2**(b-127)
     # is an E4M3 value, b in [118, 135]
