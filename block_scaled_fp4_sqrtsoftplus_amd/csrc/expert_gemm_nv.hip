@@ -31,6 +31,8 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float silu_nv(float g) { return g / (1.0f + expf(-g)); }
 
@@ -77,7 +79,7 @@ __device__ __forceinline__ bool map_tile_nv(const ExpertGemmArgs& p, int mt_max,
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(kGemmThreads) void expert_gemm_nv(ExpertGemmArgs p, int mt_max,
+__global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs p, int mt_max,
                                                                 int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_nv(ExpertGemmArgs p,
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
       wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp * 2;
+      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp * 8;
     }
   } else {
     n0 = n_tile * kG2Rows;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_nv(ExpertGemmArgs p,
     for (int t = 0; t < 4; ++t) {
       const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
       wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp * 2;
+      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp * 8;
     }
   }
   const int slot = min(m0 + col, n_e - 1);
@@ -127,53 +129,87 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_nv(ExpertGemmArgs p,
   for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   if (wave_live) {
-    // ring of four K steps: weight bytes, the two per-16 scale bytes of each
-    // weight row this lane covers, activation bytes and scale
-    uint4 A[4][4], B[4][2];
-    uint32_t SC[4][4], BS[4];
-    auto load_step = [&](int s, uint4 (&a)[4], uint32_t (&sc)[4], uint4 (&b)[2], uint32_t& bs) {
+    // Register ring of four K steps (weight and activation bytes); the
+    // scales come once per group of four steps: lane group g loads the 8
+    // scale bytes of step 4i+g of its row (32 contiguous bytes per row), and
+    // a 4x4 transpose across the lane groups hands every lane the pair of
+    // scales it needs in each of the four steps.
+    v4u A[4][4], B[4][2];
+    v2u SR[4];
+    uint32_t BSW;
+    auto load_step = [&](int s, v4u (&a)[4], v4u (&b)[2]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-        sc[t] = *reinterpret_cast<const uint16_t*>(sptr[t] + (size_t)s * 8);
-      }
-      b[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
-      b[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 16);
-      bs = bsp[s];
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
+      b[0] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128);
+      b[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
     };
-    auto compute = [&](const uint4 (&a)[4], const uint32_t (&sc)[4], const uint4 (&b)[2],
-                       uint32_t bs) {
-      const float sx = __uint_as_float(bs << 23);   // 2^(bs - 127): E8M0 as an fp32 exponent
-      const uint32_t bw[8] = {b[0].x, b[0].y, b[0].z, b[0].w, b[1].x, b[1].y, b[1].z, b[1].w};
-      h8 bo[4];
+    auto load_scales = [&](int s0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bo[j] = fp8x8_to_f16(bw[2 * j], bw[2 * j + 1]);
+      for (int t = 0; t < 4; ++t) SR[t] = *reinterpret_cast<const v2u*>(sptr[t] + (size_t)s0 * 8);
+      BSW = *reinterpret_cast<const uint32_t*>(bsp + s0);
+    };
+    // scale pairs of this lane for steps s0..s0+3: ST[t][d] = two fp16
+    auto transpose_scales = [&](uint32_t (&st)[4][4]) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const h2 ws = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[t], 1.0f, false);  // E4M3 scales
-        const uint32_t aw[4] = {a[t].x, a[t].y, a[t].z, a[t].w};
-        v4f part = {0.f, 0.f, 0.f, 0.f};
+        uint32_t r[4];
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SR[t].x, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SR[t].x, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SR[t].y, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SR[t].y, 1.0f, true));
+        // lane groups 2,3 of r[0], r[1] <-> lane groups 0,1 of r[2], r[3]
+        const auto x02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+        // odd lane groups of the first operand <-> even lane groups of the second
+        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+        st[t][0] = y01[0];
+        st[t][1] = y01[1];
+        st[t][2] = y23[0];
+        st[t][3] = y23[1];
+      }
+    };
+    auto compute = [&](const v4u (&a)[4], const uint32_t (&st)[4][4], int d, const v4u (&b)[2],
+                       uint32_t bsw) {
+      const float sx = __uint_as_float(((bsw >> (8 * d)) & 0xFFu) << 23);  // 2^(code - 127)
+      h8 bo[4];
+      bo[0] = fp8x8_to_f16(b[0].x, b[0].y);
+      bo[1] = fp8x8_to_f16(b[0].z, b[0].w);
+      bo[2] = fp8x8_to_f16(b[1].x, b[1].y);
+      bo[3] = fp8x8_to_f16(b[1].z, b[1].w);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(aw[j], j < 2 ? ws[0] : ws[1]),
-                                                        bo[j], part, 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+        const h2 ws = __builtin_bit_cast(h2, st[t][d]);
+        v4f part = {0.f, 0.f, 0.f, 0.f};
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(a[t].x, ws[0]), bo[0], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(a[t].y, ws[0]), bo[1], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(a[t].z, ws[1]), bo[2], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(a[t].w, ws[1]), bo[3], part, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(part[v], sx, acc[t][v]);
       }
     };
-    load_step(0, A[0], SC[0], B[0], BS[0]);
-    load_step(1, A[1], SC[1], B[1], BS[1]);
-    load_step(2, A[2], SC[2], B[2], BS[2]);
-    load_step(3, A[3], SC[3], B[3], BS[3]);
-    // loads past the last step re-read step S-1 (cache hits), so that no
-    // load sits behind a branch and the waits before each step stay exact
-    for (int s0 = 0; s0 < S; s0 += 4) {
+    // one group of four steps; LOAD: refill the ring with the next group
+    auto group = [&](int s0, auto load) {
+      uint32_t st[4][4];
+      transpose_scales(st);
+      const uint32_t bsw = BSW;
+      if constexpr (decltype(load)::value) load_scales(s0 + 4);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        compute(A[d], SC[d], B[d], BS[d]);
-        load_step(min(s0 + d + 4, S - 1), A[d], SC[d], B[d], BS[d]);
+        compute(A[d], st, d, B[d], bsw);
+        if constexpr (decltype(load)::value) load_step(s0 + 4 + d, A[d], B[d]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each step's refill behind its compute
       }
+    };
+    load_scales(0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      load_step(d, A[d], B[d]);
+      __builtin_amdgcn_sched_barrier(0);   // same issue order as in the loop
     }
+    for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
+    group(S - 4, std::false_type{});
   }
 
   if (MODE == 1) {
