@@ -48,7 +48,8 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_forma
     w1, w1_scale, w3, w3_scale ([E, I, H/2], [E, I, H/32]) and w2, w2_scale
     ([E, H, I/2], [E, H, I/32]); with weight_format "fp8" the FP8 expert
     layout instead: [E, N, K] E4M3 bytes with [E, N, K/128] scales; with
-    "nvfp4" the same nibbles with [E, N, K/16] E4M3 scales.
+    "nvfp4" the same nibbles with [E, N, K/16] E4M3 scales; with "w4afp8"
+    the nibbles are signed INT4 with [E, N, K/128] float32 scales.
     Returns dict: hq u8 [P, I], hs u8 [P, I/128], h fp32 [P, I] (before its
     quantization) and o float64 [P, H], all rows in sorted-pair order.
     """
@@ -59,7 +60,7 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_forma
     I = w["w1"].shape[1]
     H = w["w2"].shape[1]
     deq = {"mxfp4": quant.mxfp4_dequant, "fp8": quant.fp8_dequant,
-           "nvfp4": quant.nvfp4_dequant}[weight_format]
+           "nvfp4": quant.nvfp4_dequant, "w4afp8": quant.int4_dequant}[weight_format]
     hq = np.zeros((P, I), np.uint8)
     hs = np.zeros((P, I // 128), np.uint8)
     hf = np.zeros((P, I), np.float32)
@@ -109,7 +110,8 @@ def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0,
     """The whole MoE FFN layer on the inputs of synth.make_inputs; with
     weight_format "fp8" the routed experts run on the FP8 cast of the MXFP4
     weights (quant.fp8_experts_from_mxfp4); with "nvfp4" inp's w*_scale are
-    the NVFP4 per-16 E4M3 scales of the same nibbles.
+    the NVFP4 per-16 E4M3 scales of the same nibbles; with "w4afp8" the
+    nibbles are INT4 codes and inp's w*_scale their float32 per-128 scales.
 
     Returns dict with the routing, xq/xs, hq/hs, o, ysh (or None), y (float64)
     and y_bf16 (uint16 bit patterns)."""

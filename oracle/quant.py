@@ -17,6 +17,11 @@
                    which also names the FP8-expert checkpoint option.
 * fp8_dequant    - FP8 expert weights as that cast leaves them: E4M3 bytes
                    [N, K] with one E8M0 scale per 128 elements of K.
+* int4_dequant   - W4AFP8 expert weights: signed INT4, two per byte along K,
+                   one float32 scale per 128 elements of K
+                   ("DeepSeek-V4-Flash-0731-W4AFP8-mt" card, 量化方式 and
+                   权重约定: symmetric INT4 with group size 128,
+                   weight_scale_inv float32 [N, K/128]).
 
 Readings where the pages are silent (listed with the others in the design
 notes):
@@ -25,7 +30,9 @@ notes):
   e = -127; e is clamped to [-127, 127] and stored as the byte e + 127;
 * within a byte the even element of K sits in the low nibble;
 * the per-128 scale of the E4M3 cast is the largest of its four per-32
-  exponents.
+  exponents;
+* an INT4 nibble is two's complement (-8..7) and the float32
+  weight_scale_inv multiplies it (w = q * scale_inv).
 """
 
 import numpy as np
@@ -149,3 +156,16 @@ def fp8_experts_from_mxfp4(w):
         q, sc = zip(*(e4m3_from_mxfp4(w[n][e], w[n + "_scale"][e]) for e in range(w[n].shape[0])))
         out[n], out[n + "_scale"] = np.stack(q), np.stack(sc)
     return out
+
+
+def int4_dequant(packed, scales, block=ACT_BLOCK):
+    """Dequantize one [N, K] W4AFP8 matrix to float64: the nibbles of
+    [N, K/2] bytes read as two's complement integers -8..7 (even element of K
+    in the low nibble), times the float32 scale of their 128-element group
+    of K, scales [N, K/128]."""
+    codes = unpack_nibbles(packed).astype(np.int64)
+    q = np.where(codes >= 8, codes - 16, codes)
+    n, k = q.shape
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    assert sc.shape == (n, k // block)
+    return (q.astype(np.float64).reshape(n, k // block, block) * sc[:, :, None]).reshape(n, k)

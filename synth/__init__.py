@@ -151,3 +151,26 @@ def nvfp4_scales(wl: Workload, experts_only=None):
         for n, shape in (("w1_scale", (I, H // 16)), ("w3_scale", (I, H // 16)), ("w2_scale", (H, I // 16))):
             out[n][e] = (0x08 | r.integers(0, 8, size=shape)).astype(np.uint8)
     return out
+
+
+def w4afp8_scales(wl: Workload, experts_only=None, pow2=False):
+    """Per-128 float32 scales for W4AFP8 expert weights of workload `wl` (the
+    nibble arrays of make_inputs are reused as INT4 codes, uniform over all
+    16): 2**e * U(0.5, 0.75) with e uniform on the workload's exponent range,
+    which puts the weights' second moment near that of the MXFP4 draw; with
+    pow2 the factor U is left out (exact powers of two).  Returns w1_scale,
+    w3_scale [E, I, H/128] and w2_scale [E, H, I/128] float32."""
+    H, I, E = wl.hidden, wl.inter, wl.n_experts
+    keep = None if experts_only is None else set(int(e) for e in experts_only)
+    nexp = wl.exp_hi - wl.exp_lo + 1
+    out = {"w1_scale": np.zeros((E, I, H // 128), np.float32), "w3_scale": np.zeros((E, I, H // 128), np.float32),
+           "w2_scale": np.zeros((E, H, I // 128), np.float32)}
+    for e in range(E):
+        if keep is not None and e not in keep:
+            continue
+        r = np.random.Generator(np.random.PCG64([wl.seed, 8, e]))
+        for n, shape in (("w1_scale", (I, H // 128)), ("w3_scale", (I, H // 128)), ("w2_scale", (H, I // 128))):
+            ex = wl.exp_lo + r.integers(0, nexp, size=shape)
+            f = np.ones(shape) if pow2 else r.uniform(0.5, 0.75, size=shape)
+            out[n][e] = np.ldexp(f, ex).astype(np.float32)
+    return out

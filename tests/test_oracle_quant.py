@@ -240,3 +240,65 @@ def test_expert_layout_matches_printed_shapes():
     inp = synth.make_inputs(wl.replace(n_experts=2), tokens=1)
     assert inp["w1"].shape[1:] == shapes["w1.weight"]
     assert inp["w1_scale"].shape[1:] == (inter, hidden // 32)
+
+
+def test_int4_dequant_hand_values():
+    # two's complement nibbles, even element of K in the low nibble:
+    # 0x7F -> (-1, 7), 0x80 -> (0, -8), 0x19 -> (-7, 1), 0xF8 -> (-8, -1)
+    packed = np.zeros((1, 64), np.uint8)
+    packed[0, :4] = [0x7F, 0x80, 0x19, 0xF8]
+    scales = np.array([[0.375]], np.float32)
+    w = quant.int4_dequant(packed, scales)
+    assert w.shape == (1, 128)
+    assert w[0, :8].tolist() == [-0.375, 2.625, 0.0, -3.0, -2.625, 0.375, -3.0, -0.375]
+    assert not w[0, 8:].any()
+
+
+def test_int4_dequant_vs_library_route():
+    # numpy's int8 arithmetic shift sign-extends each nibble; scales repeat
+    # over their 128-element group
+    rng = np.random.default_rng(21)
+    n, k = 24, 640
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = rng.uniform(-3.0, 3.0, (n, k // 128)).astype(np.float32)
+    lo = (packed << 4).astype(np.uint8).view(np.int8) >> 4
+    hi = packed.view(np.int8) >> 4
+    q = np.stack([lo, hi], axis=2).reshape(n, k).astype(np.float64)
+    want = q * np.repeat(scales.astype(np.float64), 128, axis=1)
+    assert np.array_equal(quant.int4_dequant(packed, scales), want)
+    assert set(np.unique(q)) == set(range(-8, 8))
+
+
+def test_w4afp8_experts_equal_fp8_experts_for_pow2_scales():
+    # INT4 codes times power-of-two group scales are E4M3 values times an
+    # E8M0 scale per 128: the oracle's W4AFP8 expert FFN must reproduce the
+    # FP8-expert one bit for bit on those weights
+    wl = synth.WORKLOADS["tiny"].replace(hidden=512, inter=256, n_experts=5, top_k=2)
+    inp = synth.make_inputs(wl, tokens=20)
+    inp.update(synth.w4afp8_scales(wl, pow2=True))
+    f8 = {}
+    for nme in ("w1", "w3", "w2"):
+        codes = quant.unpack_nibbles(inp[nme].reshape(-1, inp[nme].shape[-1]))
+        q = np.where(codes >= 8, codes.astype(np.int64) - 16, codes).astype(np.float64)
+        f8[nme] = formats.e4m3_encode(q).reshape(inp[nme].shape[0], inp[nme].shape[1], -1)
+        e = np.log2(inp[nme + "_scale"].astype(np.float64))
+        assert np.array_equal(e, np.round(e))
+        f8[nme + "_scale"] = (e + 127).astype(np.uint8)
+    xq, xs = quant.act_quant(formats.bf16_decode(inp["x"]))
+    r = route.route(inp["x"], inp["w_gate"], k=2)
+    a = ffn.expert_ffn(xq, xs, r, f8, 2, weight_format="fp8")
+    b = ffn.expert_ffn(xq, xs, r, inp, 2, weight_format="w4afp8")
+    for key in ("hq", "hs", "h", "o"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.abs(a["o"]).max() > 0
+
+
+def test_w4afp8_scales_draw():
+    wl = synth.WORKLOADS["decode"].replace(n_experts=2)
+    s = synth.w4afp8_scales(wl)
+    assert s["w1_scale"].shape == (2, wl.inter, wl.hidden // 128) and s["w1_scale"].dtype == np.float32
+    assert s["w2_scale"].shape == (2, wl.hidden, wl.inter // 128)
+    v = s["w1_scale"].astype(np.float64)
+    m, e = np.frexp(v)          # v = m * 2**e, m in [0.5, 1)
+    assert (m >= 0.5).all() and (m < 0.75).all()
+    assert e.min() >= wl.exp_lo and e.max() <= wl.exp_hi
