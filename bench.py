@@ -36,10 +36,11 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="report graph replays of the layer (moe_graph_launch) as the step; "
                          "both are timed and reported either way")
-    ap.add_argument("--experts", choices=("mxfp4", "fp8", "nvfp4"), default="mxfp4",
+    ap.add_argument("--experts", choices=("mxfp4", "fp8", "nvfp4", "w4afp8"), default="mxfp4",
                     help="routed expert weights: the MXFP4 checkpoint format, its per-128 "
-                         "cast to FP8 (made on the GPU before timing), or NVFP4 (the same "
-                         "nibbles with synthetic per-16 E4M3 scales)")
+                         "cast to FP8 (made on the GPU before timing), NVFP4 (the same "
+                         "nibbles with synthetic per-16 E4M3 scales) or W4AFP8 (the nibbles "
+                         "as INT4 with synthetic float32 scales per 128)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -49,11 +50,12 @@ def algorithmic(wl, n_touched, fmt="mxfp4"):
     """Bytes and flops the layer must move / compute (no padding, no
     intermediates): weights of the touched experts (FP4 nibbles + E8M0
     scales per 32 of w1, w3, w2; FP8 experts: E4M3 bytes + E8M0 per 128;
-    NVFP4: nibbles + E4M3 per 16),
+    NVFP4: nibbles + E4M3 per 16; W4AFP8: INT4 nibbles + float32 per 128),
     the bf16 shared expert and gate, x in, y out."""
     T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.n_experts, wl.top_k
     per_expert = {"mxfp4": 3 * (I * H // 2 + I * H // 32), "fp8": 3 * (I * H + I * H // 128),
-                  "nvfp4": 3 * (I * H // 2 + I * H // 16)}[fmt]
+                  "nvfp4": 3 * (I * H // 2 + I * H // 16),
+                  "w4afp8": 3 * (I * H // 2 + 4 * (I * H // 128))}[fmt]
     ffn_bytes = n_touched * per_expert + T * (H + H // 128) + T * k * H * 4
     shared = 3 * I * H * 2 if wl.shared else 0
     gate = E * H * 2 if wl.mode != "hash" else 0
@@ -156,6 +158,11 @@ def main():
         for n in ("w1_scale", "w3_scale", "w2_scale"):
             w[n] = d(inp[n])
         cfg.expert_format = moe.EXPERTS_NVFP4
+    if args.experts == "w4afp8":
+        inp.update(synth.w4afp8_scales(wl))
+        for n in ("w1_scale", "w3_scale", "w2_scale"):
+            w[n] = d(inp[n])
+        cfg.expert_format = moe.EXPERTS_W4AFP8
     L = moe.Layer(cfg, w, w_gate=wg, bias=bias, shared=shared)
     y = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device=dev)
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
@@ -212,7 +219,8 @@ def main():
     ffn_ms = e0.elapsed_time(e1) / steps
 
     alg = algorithmic(wl, n_touched, args.experts)
-    src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", "expert_gemm.hip"), "rb").read()
+    src_name = {"nvfp4": "expert_gemm_nv.hip", "w4afp8": "expert_gemm_w4.hip"}.get(args.experts, "expert_gemm.hip")
+    src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", src_name), "rb").read()
     traffic = traffic_record(hashlib.sha256(src).hexdigest(),
                              wl.name + ("" if args.experts == "mxfp4" else "_" + args.experts))
     ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
@@ -228,10 +236,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / mfma_peak, 4), "traffic": traffic}
     small = wl.tokens * wl.top_k <= 32 * wl.n_experts
     fam = {"fp8": "expert_gemm_stream8" if small else "expert_gemm_kernel",
-           "nvfp4": "expert_gemm_nv",
+           "nvfp4": "expert_gemm_nv", "w4afp8": "expert_gemm_w4",
            "mxfp4": "expert_gemm_stream" if small else "expert_gemm_tile"}[args.experts]
-    roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
-                      " (+ tile prefix)")
+    if args.experts in ("nvfp4", "w4afp8"):
+        roof["kernel"] = f"routed expert FFN: {fam}<1> + {fam}<2> (+ tile prefix)"
+    else:
+        roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
+                          " (+ tile prefix)")
     roof["ms_per_call"] = round(ffn_ms, 4)
     roof["alg_bytes_per_call"] = alg["ffn_bytes"]
     roof["alg_flops_per_call"] = alg["flops_routed"]
@@ -249,7 +260,7 @@ def main():
         del src_buf, dst_buf
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, weight_format=args.experts)   # inp holds the NVFP4 scales then
+        cpu = cpu_baseline(wl, inp, weight_format=args.experts)   # inp holds the NVFP4 / W4AFP8 scales then
 
     value = wl.tokens / (ms_step * 1e-3)
     out = {
@@ -264,14 +275,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp8": "fp8e4m3 x fp8e4m3 -> f32", "mxfp4": "fp4e2m1 x fp8e4m3 -> f32",
-                  "nvfp4": "fp16(fp4e2m1 x e4m3 scale) x fp16(fp8e4m3) -> f32"}[args.experts]
+                  "nvfp4": "fp16(fp4e2m1 x e4m3 scale) x fp16(fp8e4m3) -> f32",
+                  "w4afp8": "fp8e4m3(int4 + 8) x fp8e4m3 -> f32, f32 scale per 128"}[args.experts]
                  + " (experts); bf16 -> f32 (router, shared)",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": f"{wl.name}: T={wl.tokens} H={wl.hidden} I={wl.inter} E={wl.n_experts} "
                                f"top-{wl.top_k} {'hash' if wl.mode == 'hash' else 'sqrtsoftplus'} routing"
                                f"{' + bf16 shared expert' if wl.shared else ''}"
                                f"{', FP8 experts (per-128 cast of the MXFP4 weights)' if fp8 else ''}"
-                               f"{', NVFP4 experts (per-16 E4M3 scales)' if args.experts == 'nvfp4' else ''}",
+                               f"{', NVFP4 experts (per-16 E4M3 scales)' if args.experts == 'nvfp4' else ''}"
+                               f"{', W4AFP8 experts (INT4, f32 scale per 128)' if args.experts == 'w4afp8' else ''}",
                    "tokens": wl.tokens, "experts_touched": n_touched,
                    "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2)},
         "layer": {"launch": launch,

@@ -30,7 +30,7 @@ MOE_OK = 0
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL_ARG", "MOE_ERR_BAD_SHAPE", "MOE_ERR_MISALIGNED",
                 "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_UNSUPPORTED", "MOE_ERR_ARCH", "MOE_ERR_HIP"]
 ROUTE_SQRTSOFTPLUS, ROUTE_HASH = 0, 1
-EXPERTS_MXFP4, EXPERTS_FP8, EXPERTS_NVFP4 = 0, 1, 2
+EXPERTS_MXFP4, EXPERTS_FP8, EXPERTS_NVFP4, EXPERTS_W4AFP8 = 0, 1, 2, 3
 OP_ROUTE, OP_EXPERT_FFN, OP_LAYER = 0, 1, 2
 
 
@@ -110,7 +110,7 @@ class Config:
     route_mode: int = ROUTE_SQRTSOFTPLUS
     out_fp32: int = 1
     hash_seed: int = 0
-    expert_format: int = 0          # EXPERTS_MXFP4, EXPERTS_FP8 or EXPERTS_NVFP4
+    expert_format: int = 0          # EXPERTS_MXFP4, EXPERTS_FP8, EXPERTS_NVFP4 or EXPERTS_W4AFP8
 
     def c(self):
         return MoeConfigC(self.tokens, self.hidden, self.inter, self.n_experts, self.top_k,

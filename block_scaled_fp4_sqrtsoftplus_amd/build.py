@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_fp4.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "quant_act.hip", "route.hip", "expert_gemm.hip", "expert_gemm_nv.hip",
+SOURCES = ["api.cpp", "quant_act.hip", "route.hip", "expert_gemm.hip", "expert_gemm_nv.hip", "expert_gemm_w4.hip",
            "bf16_gemm.hip", "combine.hip", "cast_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

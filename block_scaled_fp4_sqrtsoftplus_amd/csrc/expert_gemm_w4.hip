@@ -1,0 +1,293 @@
+// Grouped expert GEMMs for W4AFP8 expert weights ("DeepSeek-V4-Flash-0731-
+// W4AFP8-mt" card, 量化方式 and 权重约定: signed INT4, two per byte along K,
+// one float32 scale per 128 elements of K; FP8 E4M3 activations).
+//
+// A K step is 128 elements: one weight scale group and one activation
+// block.  The INT4 code q of nibble n (two's complement) enters the FP8 MFMA
+// as the E4M3 byte u = n ^ 8 = q + 8 in 0..15.  E4M3 codes 0..15 encode
+// exactly u * 2^-9 (subnormals below 8, exponent field 1 from 8 up), so with
+// a block scale of 2^9 on that operand the step's MFMA gives
+// sum_k (q_k + 8) x_k.  One more MFMA per step, against a constant operand of
+// code 8, gives 8 sum_k x_k per token; it is subtracted before the row's
+// float32 group scale multiplies the step's result into the accumulator.
+// The products u * x are exact (4 x 4 significant bits) and the per-step
+// sums are fp32, as in the other expert GEMMs.
+//
+// MFMA roles are swapped relative to the FP4 kernels: A = activations (rows
+// = the m-tile's 16 pairs, their E8M0 scale per 128 as A's block scale),
+// B = weights (columns = 16 weight rows), so that the four results a lane
+// holds share one weight row and one group scale.  Lane l (c = l % 16,
+// g = l / 16) supplies token c and weight row c of the tile; lane group g
+// takes elements 32g .. 32g+31 of the step: 16 bytes of the weight row and
+// 32 bytes of the activation row.  The unpacked weight bytes come out as
+// the even elements of each 8 followed by the odd ones, and the activation
+// bytes are permuted the same way (both operands share the MFMA's K slots,
+// so any common order sums the same products).  D: lane l holds
+// D[4g + v][c] -- token 4g + v, weight row c.
+//
+// Work split, m-tiles of 16 pairs, 4 waves x 64 weight rows, the register
+// ring of four K steps, the per-group scale loads and the XCD-aware tile map
+// follow the NVFP4 expert GEMMs; K must be a multiple of 512.
+#include "moe_internal.h"
+
+#include <type_traits>
+
+namespace moe {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float silu_w4(float g) { return g / (1.0f + expf(-g)); }
+
+// D = A . B with E8M0 block scales sa (A) and sb (B), from zero.  The asm
+// leaves 2 wait states between the VALU instructions that build the
+// operands and the MFMA (the compiler cannot insert them in front of an asm;
+// without them the MFMA read a stale B register), and the scale registers
+// and the result untouched for 32 wait states after it, as in the FP4
+// kernels.
+__device__ __forceinline__ v4f mfma_w4(const v8i& a, const v8i& b, int sa, int sb) {
+  v4f d;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : "=&v"(d)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  return d;
+}
+
+// 32 INT4 codes (16 bytes of a weight row) -> the E4M3 bytes q + 8 of the
+// B operand: dword 2i holds elements 8i, 8i+2, 8i+4, 8i+6, dword 2i+1 the
+// odd ones 8i+1 .. 8i+7
+__device__ __forceinline__ v8i int4_operand(const v4u& w) {
+  const uint32_t y0 = w.x ^ 0x88888888u, y1 = w.y ^ 0x88888888u;
+  const uint32_t y2 = w.z ^ 0x88888888u, y3 = w.w ^ 0x88888888u;
+  return v8i{(int)(y0 & 0x0F0F0F0Fu), (int)((y0 >> 4) & 0x0F0F0F0Fu),
+             (int)(y1 & 0x0F0F0F0Fu), (int)((y1 >> 4) & 0x0F0F0F0Fu),
+             (int)(y2 & 0x0F0F0F0Fu), (int)((y2 >> 4) & 0x0F0F0F0Fu),
+             (int)(y3 & 0x0F0F0F0Fu), (int)((y3 >> 4) & 0x0F0F0F0Fu)};
+}
+
+// 32 activation bytes (elements 0..31 in order) -> the same slot order
+__device__ __forceinline__ v8i act_operand(const v4u& b0, const v4u& b1) {
+  const uint32_t a[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  v8i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = (int)__builtin_amdgcn_perm(a[2 * i + 1], a[2 * i], 0x06040200u);
+    r[2 * i + 1] = (int)__builtin_amdgcn_perm(a[2 * i + 1], a[2 * i], 0x07050301u);
+  }
+  return r;
+}
+
+__device__ __forceinline__ bool map_tile_w4(const ExpertGemmArgs& p, int mt_max, int n_tiles,
+                                            int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int w = (b & 7) * (G >> 3) + (b >> 3);   // XCD-aware: consecutive ids per XCD
+  n_tile = w / mt_max;
+  const int mt = w - n_tile * mt_max;
+  if (n_tile >= n_tiles) return false;
+  if (mt >= p.mtile_off[p.E]) return false;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
+  }
+  e = lo;
+  m0 = (mt - p.mtile_off[e]) * 16;
+  off_e = p.expert_offsets[e];
+  n_e = p.expert_offsets[e + 1] - off_e;
+  return true;
+}
+
+constexpr int kW4ScaleB = 127 + 9;        // E8M0 2^9: undoes the 2^-9 of the INT4 bytes
+
+}  // namespace
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs p, int mt_max,
+                                                                   int n_tiles) {
+  __shared__ float red[4][16];
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile_w4(p, mt_max, n_tiles, n_tile, e, m0, off_e, n_e)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int S = K / 128;                    // a multiple of 4
+  const size_t wrow_bytes = (size_t)K / 2;
+
+  const uint8_t* wptr[4];
+  const float* sptr[4];
+  int n0;
+  bool wave_live = true;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const uint8_t* base = (t < 2) ? p.w : p.w3;
+      const float* sbase = reinterpret_cast<const float*>((t < 2) ? p.w_scale : p.w3_scale);
+      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = sbase + ((size_t)e * N + row) * S;
+    }
+  } else {
+    n0 = n_tile * kG2Rows;
+    wave_live = (n0 + 64 * wv) < N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
+      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      sptr[t] = reinterpret_cast<const float*>(p.w_scale) + ((size_t)e * N + row) * S;
+    }
+  }
+  const int slot = min(m0 + col, n_e - 1);
+  const int64_t brow = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
+                                   : (int64_t)(off_e + slot);
+  const uint8_t* bptr = p.a + brow * K + 32 * grp;
+  const uint8_t* bsp = p.a_scale + brow * S;
+
+  v4f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (wave_live) {
+    // register ring of four K steps (weight and activation bytes); the
+    // group scales and the activation scale bytes come once per four steps
+    v4u A[4][4], B[4][2];
+    v4u SW[4];                 // float32 scales of steps s0..s0+3, per tile
+    uint32_t BSW;              // activation scale bytes of steps s0..s0+3
+    const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
+                        0x08080808, 0x08080808, 0x08080808, 0x08080808};
+    auto load_step = [&](int s, v4u (&a)[4], v4u (&b)[2]) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
+      b[0] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128);
+      b[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
+    };
+    auto load_scales = [&](int s0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) SW[t] = *reinterpret_cast<const v4u*>(sptr[t] + s0);
+      BSW = *reinterpret_cast<const uint32_t*>(bsp + s0);
+    };
+    auto compute = [&](const v4u (&a)[4], const v4u (&sw)[4], int d, const v4u (&b)[2],
+                       uint32_t bsw) {
+      const int sa = (int)((bsw >> (8 * d)) & 0xFFu);
+      const v8i xa = act_operand(b[0], b[1]);
+      const v4f corr = mfma_w4(xa, eights, sa, kW4ScaleB);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4f part = mfma_w4(xa, int4_operand(a[t]), sa, kW4ScaleB);
+        const float s = __uint_as_float(sw[t][d]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(part[v] - corr[v], s, acc[t][v]);
+      }
+    };
+    // one group of four steps; LOAD: refill the ring with the next group
+    auto group = [&](int s0, auto load) {
+      v4u sw[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sw[t] = SW[t];
+      const uint32_t bsw = BSW;
+      if constexpr (decltype(load)::value) load_scales(s0 + 4);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        compute(A[d], sw, d, B[d], bsw);
+        if constexpr (decltype(load)::value) load_step(s0 + 4 + d, A[d], B[d]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each step's refill behind its compute
+      }
+    };
+    load_scales(0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      load_step(d, A[d], B[d]);
+      __builtin_amdgcn_sched_barrier(0);     // same issue order as in the loop
+    }
+    for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
+    group(S - 4, std::false_type{});
+  }
+
+  // lane holds acc[t][v] = output (token 4 * grp + v, weight row col of tile t)
+  if (MODE == 1) {
+    float h[2][4];
+    float amax[4];
+    const float lim = p.limit;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      amax[v] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
+        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
+        const float hv = silu_w4(g) * u;
+        h[tt][v] = hv;
+        amax[v] = fmaxf(amax[v], fabsf(hv));
+      }
+      // over the 16 weight rows of the lane group
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) amax[v] = fmaxf(amax[v], __shfl_xor(amax[v], m));
+    }
+    if (col == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wv][4 * grp + v] = amax[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 4 * grp + v;
+      if (m0 + tok >= n_e) continue;
+      const float bmax = fmaxf(fmaxf(red[0][tok], red[1][tok]), fmaxf(red[2][tok], red[3][tok]));
+      const int ex = pow2_scale_exp(bmax);
+      const size_t row = (size_t)(off_e + m0 + tok);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        p.hq[row * N + n0 + 32 * wv + 16 * tt + col] = (uint8_t)e4m3_rne(ldexpf(h[tt][v], -ex));
+      if (wv == 0 && col == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+    }
+  } else {
+    if (!wave_live) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 4 * grp + v;
+      if (m0 + tok >= n_e) continue;
+      const size_t row = (size_t)(off_e + m0 + tok);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const size_t c = (size_t)n0 + 64 * wv + 16 * t + col;
+        if (p.out_fp32)
+          reinterpret_cast<float*>(p.out)[row * N + c] = acc[t][v];
+        else
+          reinterpret_cast<uint16_t*>(p.out)[row * N + c] = (uint16_t)f32_to_bf16(acc[t][v]);
+      }
+    }
+  }
+}
+
+static unsigned pad8_w4(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
+
+template <int MODE>
+static hipError_t launch_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
+  if (a.K % 512) return hipErrorInvalidValue;
+  const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
+  const unsigned grid = pad8_w4((int64_t)n_tiles * mt_max);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((expert_gemm_w4<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a, mt_max,
+                     n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
+  return launch_w4<1>(a, mt_max, st);
+}
+hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
+  return launch_w4<2>(a, mt_max, st);
+}
+
+}  // namespace moe

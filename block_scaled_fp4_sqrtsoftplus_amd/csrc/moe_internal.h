@@ -122,6 +122,7 @@ struct ExpertGemmArgs {
   void* out;                 // GEMM2 out
   int out_fp32;
   int fp8w;                  // weights: 0 MXFP4 ([N, K/2] + [N, K/32]), 1 FP8 ([N, K] + [N, K/128])
+                             // (NVFP4 and W4AFP8 have launchers of their own)
 };
 
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
@@ -130,6 +131,9 @@ hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipS
 // NVFP4 weights (E4M3 scale per 16), m-tiles of 16 pairs, K % 512 == 0.
 hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
+// W4AFP8 weights (INT4 + float32 scale per 128), m-tiles of 16 pairs, K % 512 == 0.
+hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
+hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
 
 // MXFP4 [rows, K/2] + [rows, K/32] -> FP8 E4M3 [rows, K] + E8M0 [rows, K/128].
 hipError_t launch_cast_fp8(const uint8_t* w, const uint8_t* ws, uint8_t* q, uint8_t* qs,

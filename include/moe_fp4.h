@@ -91,9 +91,12 @@ typedef enum moe_route_mode {
 typedef enum moe_expert_format {
   MOE_EXPERTS_MXFP4 = 0,      /* E2M1 nibbles + E8M0 per 32 (the checkpoint) */
   MOE_EXPERTS_FP8 = 1,        /* E4M3 bytes + E8M0 per 128                   */
-  MOE_EXPERTS_NVFP4 = 2       /* E2M1 nibbles + E4M3 per 16 (阶段三导出);
+  MOE_EXPERTS_NVFP4 = 2,      /* E2M1 nibbles + E4M3 per 16 (阶段三导出);
                                  needs hidden % 512 == 0 and inter % 512 == 0,
                                  else MOE_ERR_UNSUPPORTED                   */
+  MOE_EXPERTS_W4AFP8 = 3      /* signed INT4 + float32 per 128
+                                 ("DeepSeek-V4-Flash-0731-W4AFP8-mt" card,
+                                 量化方式 / 权重约定); same size limits as NVFP4 */
 } moe_expert_format;
 
 typedef enum moe_op {
@@ -131,7 +134,11 @@ typedef struct moe_config {
  * E4M3 bytes, scales [E, I, H/128] and [E, H, I/128] E8M0 bytes
  * (moe_expert_cast_fp8 writes them).  With MOE_EXPERTS_NVFP4: the nibble
  * arrays as for MXFP4, scales [E, I, H/16] and [E, H, I/16] E4M3 bytes
- * (one per 16 elements of K, no per-tensor scale).                     */
+ * (one per 16 elements of K, no per-tensor scale).  With
+ * MOE_EXPERTS_W4AFP8: the same byte arrays hold two's complement INT4
+ * pairs (even element of K in the low nibble) and the scale pointers point
+ * to float32 arrays [E, I, H/128] and [E, H, I/128], 16-byte aligned, that
+ * multiply the integers (the checkpoint's weight_scale_inv).            */
 typedef struct moe_expert_weights {
   const uint8_t* w1;
   const uint8_t* w1_scale;

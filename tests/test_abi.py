@@ -129,7 +129,7 @@ def test_graph_argument_errors():
 
 def test_expert_format_and_cast_argument_errors():
     c = _cfg()
-    c.expert_format = 3
+    c.expert_format = 4
     assert lib.moe_workspace_size(ctypes.byref(c), moe.OP_LAYER) == 0
     assert lib.moe_layer(ctypes.byref(c), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
                          1 << 40, None) == 2
@@ -141,6 +141,13 @@ def test_expert_format_and_cast_argument_errors():
     assert lib.moe_layer(ctypes.byref(n), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
                          1 << 40, None) == 5
     n.inter = 512
+    assert lib.moe_workspace_size(ctypes.byref(n), moe.OP_LAYER) > 0
+    # and so do W4AFP8 experts
+    n = _cfg(hidden=640, inter=512)
+    n.expert_format = moe.EXPERTS_W4AFP8
+    assert lib.moe_layer(ctypes.byref(n), 16, 16, None, None, ctypes.byref(_w()), None, 16, None, 16,
+                         1 << 40, None) == 5
+    n.hidden = 1024
     assert lib.moe_workspace_size(ctypes.byref(n), moe.OP_LAYER) > 0
     # cast: NULL / misaligned source or destination arrays
     assert lib.moe_expert_cast_fp8(ctypes.byref(c), None, ctypes.byref(_w()), None) == 1

@@ -8,8 +8,13 @@ next VALU instruction has been measured harmless on gfx950.)  This test
 builds the GEMM source for gfx950 and checks, in the generated AMD assembly,
 that no VALU instruction writes a scale register or the accumulator of a
 scaled MFMA within 32 wait states of it, and that nothing but another MFMA
-reads an MFMA's accumulator within that distance.  CPU-only: hipcc
-cross-compiles."""
+reads an MFMA's accumulator within that distance.  Before the MFMA, the
+hardware needs wait states between a VALU write of a source register (A, B
+or a scale) and the MFMA's read of it -- the compiler puts two there for the
+builtin -- which it cannot insert in front of an asm MFMA either: the check
+asks for at least PRE wait states there.  (A W4AFP8 GEMM whose B operand was
+written by the VALU instruction right before the asm MFMA read a stale value
+on gfx950.)  CPU-only: hipcc cross-compiles."""
 
 import os
 import re
@@ -20,9 +25,11 @@ import tempfile
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", "expert_gemm.hip")
+CSRC = os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc")
+SOURCES = ["expert_gemm.hip", "expert_gemm_w4.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 NEED = 32
+PRE = 2
 
 
 def _regs(op):
@@ -44,19 +51,53 @@ def _functions(asm):
     return funcs
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-def test_scaled_mfma_operands_untouched_for_32_wait_states():
+def _compile(src):
     tmp = tempfile.mkdtemp()
     try:
         cmd = [HIPCC, "--offload-arch=gfx950", "--cuda-device-only", "-S", "-O3", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off",
-               "-I", os.path.join(ROOT, "include"), "-I", os.path.dirname(SRC), SRC,
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, src),
                "-o", os.path.join(tmp, "eg.s")]
         subprocess.run(cmd, check=True, capture_output=True)
-        asm = open(os.path.join(tmp, "eg.s")).read()
+        return open(os.path.join(tmp, "eg.s")).read()
     finally:
         shutil.rmtree(tmp)
-    funcs = _functions(asm)
+
+
+def _written(t):
+    """Registers a VALU instruction writes (none for other instructions)."""
+    if not t.startswith("v_") or t.startswith("v_mfma"):
+        return set()
+    parts = t.split(None, 1)
+    return _regs(parts[1].split(",")[0].strip()) if len(parts) == 2 else set()
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+@pytest.mark.parametrize("src", SOURCES)
+def test_scaled_mfma_sources_settled_before_issue(src):
+    funcs = _functions(_compile(src))
+    total = 0
+    for name, ins in funcs.items():
+        for i, s in enumerate(ins):
+            if not s.startswith("v_mfma_scale"):
+                continue
+            total += 1
+            ops = [o.strip() for o in s.split(None, 1)[1].split(" op_sel")[0].split(",")]
+            srcs = _regs(ops[1]) | _regs(ops[2]) | _regs(ops[4]) | _regs(ops[5])
+            ws = 0
+            for t in reversed(ins[:i]):
+                if ws >= PRE:
+                    break
+                assert not (_written(t) & srcs), f"{name}: '{t}' {ws} wait states before '{s}'"
+                m = re.match(r"s_nop (\d+)", t)
+                ws += int(m.group(1)) + 1 if m else 1
+    assert total > 0
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+@pytest.mark.parametrize("src", SOURCES)
+def test_scaled_mfma_operands_untouched_for_32_wait_states(src):
+    funcs = _functions(_compile(src))
     total = 0
     for name, ins in funcs.items():
         for i, s in enumerate(ins):
