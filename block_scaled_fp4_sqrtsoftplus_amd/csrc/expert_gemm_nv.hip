@@ -78,7 +78,18 @@ __device__ __forceinline__ bool map_tile_nv(const ExpertGemmArgs& p, int mt_max,
 
 }  // namespace
 
-template <int MODE>
+// LDS row stride of the staged scale lines: 256 bytes (K = 4096) + 16, so
+// that the 16 rows a wave reads at one K offset fall in distinct banks
+constexpr int kNvScaleStride = 272;
+__shared__ uint32_t nv_lds[4 * 4 * 16 * kNvScaleStride / 4];   // 69632 bytes
+
+// LINE: K <= 4096 -- each wave copies the whole scale lines of its 64 weight
+// rows (at most 256 bytes each) to its own LDS area once, and every step
+// reads its two bytes per row from there.  Read from HBM a group of steps at
+// a time (32 of a line's bytes every four steps), the lines were fetched
+// again and again (~25% more HBM reads at decode).  Longer K loads each
+// group's scales with the group (see below).
+template <int MODE, bool LINE>
 __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs p, int mt_max,
                                                                 int n_tiles) {
   __shared__ float red[4][16];
@@ -95,7 +106,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
   const size_t srow_bytes = (size_t)K / 16;
 
   const uint8_t* wptr[4];
-  const uint8_t* sptr[4];
+  const uint8_t* sptr[4];   // + 8 * grp
+  const uint8_t* srow[4];   // scale line of the lane's weight row
   int n0;
   bool wave_live = true;
   if (MODE == 1) {
@@ -106,7 +118,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
       wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes + grp * 8;
+      srow[t] = sbase + ((size_t)e * N + row) * srow_bytes;
+      sptr[t] = srow[t] + grp * 8;
     }
   } else {
     n0 = n_tile * kG2Rows;
@@ -115,7 +128,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
     for (int t = 0; t < 4; ++t) {
       const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
       wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes + grp * 8;
+      srow[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+      sptr[t] = srow[t] + grp * 8;
     }
   }
   const int slot = min(m0 + col, n_e - 1);
@@ -137,6 +151,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
     v4u A[4][4], B[4][2];
     v2u SR[4];
     uint32_t BSW;
+    // LINE: [tile][row][byte] scale lines of this wave's rows
+    uint8_t* const lds_sc = LINE ? reinterpret_cast<uint8_t*>(nv_lds) + wv * (4 * 16 * kNvScaleStride) : nullptr;
     auto load_step = [&](int s, v4u (&a)[4], v4u (&b)[2]) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
@@ -144,8 +160,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
       b[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
     };
     auto load_scales = [&](int s0) {
+      if constexpr (!LINE) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) SR[t] = *reinterpret_cast<const v2u*>(sptr[t] + (size_t)s0 * 8);
+        for (int t = 0; t < 4; ++t) SR[t] = *reinterpret_cast<const v2u*>(sptr[t] + (size_t)s0 * 8);
+      }
       BSW = *reinterpret_cast<const uint32_t*>(bsp + s0);
     };
     // scale pairs of this lane for steps s0..s0+3: ST[t][d] = two fp16
@@ -192,21 +210,61 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
     // one group of four steps; LOAD: refill the ring with the next group
     auto group = [&](int s0, auto load) {
       uint32_t st[4][4];
-      transpose_scales(st);
+      if constexpr (LINE) {
+        // the lane's pair of scales (scale groups 2 grp, 2 grp + 1) per step
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t raw = *reinterpret_cast<const uint16_t*>(
+                lds_sc + (t * 16 + col) * kNvScaleStride + 8 * (s0 + d) + 2 * grp);
+            st[t][d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
+          }
+      } else {
+        transpose_scales(st);
+      }
       const uint32_t bsw = BSW;
       if constexpr (decltype(load)::value) load_scales(s0 + 4);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         compute(A[d], st, d, B[d], bsw);
-        if constexpr (decltype(load)::value) load_step(s0 + 4 + d, A[d], B[d]);
-        __builtin_amdgcn_sched_barrier(0);   // keep each step's refill behind its compute
+        // refill two steps at a time, back to back: the two 64-byte halves
+        // of a weight row's 128-byte line are then requested together, and
+        // the second one meets the first one's line fill (requested a step
+        // apart, the second half missed again: ~25% more HBM reads)
+        if constexpr (decltype(load)::value) {
+          if (d & 1) {
+            load_step(s0 + 3 + d, A[d - 1], B[d - 1]);
+            load_step(s0 + 4 + d, A[d], B[d]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep each refill behind its compute
       }
     };
+    v4u SL[4][4];
+    if constexpr (LINE) {
+      // lane group g copies bytes 64 g .. 64 g + 63 of each line; pieces past
+      // the line's end clamp to its last 16 bytes (same data, same place)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          SL[t][j] = *reinterpret_cast<const v4u*>(srow[t] + min(64 * grp + 16 * j, 8 * S - 16));
+      __builtin_amdgcn_sched_barrier(0);
+    }
     load_scales(0);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       load_step(d, A[d], B[d]);
       __builtin_amdgcn_sched_barrier(0);   // same issue order as in the loop
+    }
+    if constexpr (LINE) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<v4u*>(lds_sc + (t * 16 + col) * kNvScaleStride +
+                                  min(64 * grp + 16 * j, 8 * S - 16)) = SL[t][j];
     }
     for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
     group(S - 4, std::false_type{});
@@ -270,8 +328,12 @@ static hipError_t launch_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st)
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8_nv((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((expert_gemm_nv<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a, mt_max,
-                     n_tiles);
+  if (a.K <= 4096)
+    hipLaunchKernelGGL((expert_gemm_nv<MODE, true>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
+  else
+    hipLaunchKernelGGL((expert_gemm_nv<MODE, false>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
   return hipGetLastError();
 }
 

@@ -109,7 +109,13 @@ constexpr int kW4ScaleB = 127 + 9;        // E8M0 2^9: undoes the 2^-9 of the IN
 
 }  // namespace
 
-template <int MODE>
+// LINE: K <= 4096 -- each weight row's whole scale line (at most 128 bytes)
+// is loaded once, a quarter per lane group, and each group of four steps
+// takes its four scales from the lane group holding them (ds_bpermute).
+// Read a piece at a time over the K loop, the line was fetched again and
+// again (~25% more HBM reads at decode).  Longer K loads each group's four
+// scales with the group.
+template <int MODE, bool LINE>
 __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs p, int mt_max,
                                                                    int n_tiles) {
   __shared__ float red[4][16];
@@ -162,7 +168,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     // register ring of four K steps (weight and activation bytes); the
     // group scales and the activation scale bytes come once per four steps
     v4u A[4][4], B[4][2];
-    v4u SW[4];                 // float32 scales of steps s0..s0+3, per tile
+    v4u SW[4];                 // !LINE: float32 scales of steps s0..s0+3, per tile
+    v4u SL[4][2];              // LINE: scales of steps 8 grp .. 8 grp + 7, per tile
     uint32_t BSW;              // activation scale bytes of steps s0..s0+3
     const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
                         0x08080808, 0x08080808, 0x08080808, 0x08080808};
@@ -173,8 +180,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
       b[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
     };
     auto load_scales = [&](int s0) {
+      if constexpr (!LINE) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) SW[t] = *reinterpret_cast<const v4u*>(sptr[t] + s0);
+        for (int t = 0; t < 4; ++t) SW[t] = *reinterpret_cast<const v4u*>(sptr[t] + s0);
+      }
       BSW = *reinterpret_cast<const uint32_t*>(bsp + s0);
     };
     auto compute = [&](const v4u (&a)[4], const v4u (&sw)[4], int d, const v4u (&b)[2],
@@ -193,17 +202,44 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     // one group of four steps; LOAD: refill the ring with the next group
     auto group = [&](int s0, auto load) {
       v4u sw[4];
+      if constexpr (LINE) {
+        const int src = (16 * (s0 >> 3) + col) * 4;   // lane group s0 / 8 holds them
+        const bool hi = (s0 & 4) != 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sw[t] = SW[t];
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            sw[t][d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(hi ? SL[t][1][d] : SL[t][0][d]));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sw[t] = SW[t];
+      }
       const uint32_t bsw = BSW;
       if constexpr (decltype(load)::value) load_scales(s0 + 4);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         compute(A[d], sw, d, B[d], bsw);
-        if constexpr (decltype(load)::value) load_step(s0 + 4 + d, A[d], B[d]);
-        __builtin_amdgcn_sched_barrier(0);   // keep each step's refill behind its compute
+        // refill two steps at a time, back to back: the two 64-byte halves
+        // of a weight row's 128-byte line are then requested together, and
+        // the second one meets the first one's line fill (requested a step
+        // apart, the second half missed again: ~25% more HBM reads)
+        if constexpr (decltype(load)::value) {
+          if (d & 1) {
+            load_step(s0 + 3 + d, A[d - 1], B[d - 1]);
+            load_step(s0 + 4 + d, A[d], B[d]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep each refill behind its compute
       }
     };
+    if constexpr (LINE) {
+      // steps past the last one clamp to it (in bounds, never used)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        SL[t][0] = *reinterpret_cast<const v4u*>(sptr[t] + min(8 * grp, S - 4));
+        SL[t][1] = *reinterpret_cast<const v4u*>(sptr[t] + min(8 * grp + 4, S - 4));
+      }
+    }
     load_scales(0);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -278,8 +314,12 @@ static hipError_t launch_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st)
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8_w4((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((expert_gemm_w4<MODE>), dim3(grid), dim3(kGemmThreads), 0, st, a, mt_max,
-                     n_tiles);
+  if (a.K <= 4096)
+    hipLaunchKernelGGL((expert_gemm_w4<MODE, true>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
+  else
+    hipLaunchKernelGGL((expert_gemm_w4<MODE, false>), dim3(grid), dim3(kGemmThreads), 0, st, a,
+                       mt_max, n_tiles);
   return hipGetLastError();
 }
 
