@@ -148,6 +148,9 @@ struct SideStream {
 };
 SideStream g_side[64];
 
+// Batches from which moe_layer starts the shared expert before routing.
+constexpr int64_t kEarlyForkTokens = 256;
+
 moe_status side_stream(SideStream*& out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
@@ -450,18 +453,16 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
     return enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st);
 
   // Caller's stream: quantize x, route, routed experts, combine.  The shared
-  // expert (which needs only x) forks onto the side stream once routing is
-  // enqueued -- so it overlaps the bandwidth-bound expert GEMMs rather than
-  // the latency-bound routing kernels -- and joins before the combine.
-  MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
-  bool tiles_done = false;
-  if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
-                         l.ffn.mtile_off, &tiles_done)) != MOE_OK)
-    return s;
+  // expert (which needs only x) runs on the side stream and joins before the
+  // combine.  Small batches fork it once routing is enqueued, so that it
+  // overlaps the bandwidth-bound expert GEMMs rather than the latency-bound
+  // routing kernels (forking first cost 2% at T = 64); batches of at least
+  // kEarlyForkTokens fork it first, where its GEMMs are long enough to fill
+  // the routing kernels' idle GPU (7% less layer time at T = 4096).
   const float* ysh = nullptr;
   std::unique_lock<std::mutex> lock;
   SideStream* side = nullptr;
-  if (shared) {
+  auto fork_shared = [&]() -> moe_status {
     if ((s = side_stream(side)) != MOE_OK) return s;
     lock = std::unique_lock<std::mutex>(side->mu);
     if ((s = side_init_locked(*side)) != MOE_OK) return s;
@@ -473,7 +474,16 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
     MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, c.tokens, c.hidden, c.inter, ss));
     MOE_TRY(hipEventRecord(side->join, ss));
     ysh = l.ysh;
-  }
+    return MOE_OK;
+  };
+  const bool early_fork = shared && c.tokens >= kEarlyForkTokens;
+  if (early_fork && (s = fork_shared()) != MOE_OK) return s;
+  MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
+  bool tiles_done = false;
+  if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
+                         l.ffn.mtile_off, &tiles_done)) != MOE_OK)
+    return s;
+  if (shared && !early_fork && (s = fork_shared()) != MOE_OK) return s;
   if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,
                        tiles_done)) != MOE_OK)
     return s;
