@@ -238,6 +238,11 @@ def _check_o(o, hq, hs, ref, r, absw2, tau=None):
     ("decode", 600, dict(hidden=1024, inter=1024, n_experts=8, top_k=2)),
     ("decode", 300, dict(hidden=2048, inter=4096, n_experts=4, top_k=2)),
     ("decode", 400, dict(n_experts=8, top_k=2)),
+    # largest K on each GEMM (hidden / inter 16384), and a V4-Pro-sized layer
+    # (H = 7168, I = 3072: K outside the streaming kernels' set)
+    ("decode", 4, dict(hidden=16384, inter=512, n_experts=3, top_k=2)),
+    ("decode", 4, dict(hidden=512, inter=16384, n_experts=3, top_k=2)),
+    ("decode", 6, dict(hidden=7168, inter=3072, n_experts=16, top_k=6)),
 ])
 def test_expert_ffn_parity(shape):
     name, tokens, over = shape

@@ -48,6 +48,7 @@ def check_routing_valid(r, T, k, E):
     ("tiny", 150, dict(hidden=256, inter=256, n_experts=4, top_k=2, shared=True)),
     ("tiny", 33, dict(mode="hash", n_experts=20, top_k=6, hidden=384, inter=256, shared=True)),
     ("tiny", 1, dict(n_experts=8, top_k=8)),
+    ("tiny", 20, dict(n_experts=512, top_k=8, hidden=256, inter=128)),   # largest E and k
     ("decode", 5, dict(n_experts=12)),
     ("decode", 300, dict(hidden=1024, inter=1024, n_experts=4, top_k=2, shared=True)),
 ])

@@ -29,6 +29,7 @@ def _nv_inputs(wl, tokens):
     ("decode", 10, dict(hidden=1024, inter=1024, n_experts=8)),           # K = 1024
     ("tiny", 37, dict(hidden=512, inter=512, n_experts=12, top_k=3)),     # K = 512: one group of steps
     ("tiny", 200, dict(hidden=512, inter=1024, n_experts=6, top_k=2)),    # many 16-pair tiles per expert
+    ("decode", 6, dict(hidden=4608, inter=5120, n_experts=4, top_k=2)),   # K > 4096: scales loaded per group
 ])
 def test_nvfp4_expert_ffn_parity(shape):
     name, tokens, over = shape

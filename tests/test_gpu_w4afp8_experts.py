@@ -30,6 +30,7 @@ def _w4_inputs(wl, tokens):
     ("tiny", 37, dict(hidden=512, inter=512, n_experts=12, top_k=3)),     # K = 512: one group of steps
     ("tiny", 200, dict(hidden=512, inter=1024, n_experts=6, top_k=2)),    # many 16-pair tiles per expert
     ("decode", 7, dict(hidden=1536, inter=2560, n_experts=5, top_k=2)),   # K = 1536 / 2560: 3 and 5 step groups
+    ("decode", 6, dict(hidden=4608, inter=5120, n_experts=4, top_k=2)),   # K > 4096: scales loaded per group
 ])
 def test_w4afp8_expert_ffn_parity(shape):
     name, tokens, over = shape
