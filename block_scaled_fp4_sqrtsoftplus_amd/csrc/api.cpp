@@ -62,13 +62,20 @@ struct RouteWs {
   float* logits;
   int32_t* mtile_off;  // m-tile prefix written by the single-workgroup routing
 };
+// Partial sums the router GEMM leaves for the top-k kernel to add (1: the
+// logits themselves).
+int router_partials(const moe_config& c) {
+  const int small = router_splits(c.tokens, c.hidden);
+  return small > 1 ? small : router_tile_splits(c.tokens, c.hidden, c.n_experts);
+}
+
 RouteWs carve_route(Carver& cv, const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
   RouteWs r;
   r.perm_scratch = cv.take<int32_t>(permute_scratch_bytes(P, c.n_experts) / sizeof(int32_t) + 1);
-  // logits, or their split partial sums for small batches
+  // logits, or their split partial sums
   r.logits = cv.take<float>(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS
-                                ? (size_t)c.tokens * c.n_experts * router_splits(c.tokens, c.hidden)
+                                ? (size_t)c.tokens * c.n_experts * router_partials(c)
                                 : 0);
   r.mtile_off = cv.take<int32_t>(c.n_experts + 1);
   return r;
@@ -208,8 +215,9 @@ int choose_bm(const moe_config& c) {
 }
 
 // Routing (S1-S3).  Small batches run the single-workgroup permutation
-// kernel, which also writes the grouped GEMMs' m-tile prefix to `mtile_off`
-// (when given); the return flag says whether it did.
+// kernel, larger ones the histogram / scan / scatter kernels; either also
+// writes the grouped GEMMs' m-tile prefix to `mtile_off` (when given), and
+// the return flag says whether it did.
 moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t* wg,
                          const float* bias, const int64_t* ids, const float* logits_in,
                          float* logits_out, const moe_routing& r, const RouteWs& ws,
@@ -221,6 +229,11 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
                               r.topk_idx, r.topk_w, st));
   } else if (logits_in) {
     MOE_TRY(launch_score_topk(logits_in, 1, logits_out, bias, T, c.n_experts, c.top_k,
+                              c.route_scale, r.topk_idx, r.topk_w, st));
+  } else if (router_tile_splits(T, c.hidden, c.n_experts) > 1) {
+    const int ks = router_tile_splits(T, c.hidden, c.n_experts);
+    MOE_TRY(launch_router_tile_split(x, wg, ws.logits, T, c.hidden, c.n_experts, ks, st));
+    MOE_TRY(launch_score_topk(ws.logits, ks, logits_out, bias, T, c.n_experts, c.top_k,
                               c.route_scale, r.topk_idx, r.topk_w, st));
   } else if (router_splits(T, c.hidden) > 1) {
     MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, st));
@@ -239,7 +252,8 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
     return MOE_OK;
   }
   MOE_TRY(launch_permute(r.topk_idx, P, c.n_experts, r.expert_offsets, r.sorted_pairs,
-                         r.pair_pos, ws.perm_scratch, st));
+                         r.pair_pos, ws.perm_scratch, choose_bm(c), mtile_off, st));
+  if (tiles_done) *tiles_done = mtile_off != nullptr;
   return MOE_OK;
 }
 
@@ -458,7 +472,8 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   // overlaps the bandwidth-bound expert GEMMs rather than the latency-bound
   // routing kernels (forking first cost 2% at T = 64); batches of at least
   // kEarlyForkTokens fork it first, where its GEMMs are long enough to fill
-  // the routing kernels' idle GPU (7% less layer time at T = 4096).
+  // the GPU the routing kernels leave idle (1.6% less layer time at
+  // T = 32768, the same at T = 4096).
   const float* ysh = nullptr;
   std::unique_lock<std::mutex> lock;
   SideStream* side = nullptr;

@@ -366,6 +366,8 @@ __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __re
 //              the same columns; wave (wm, wn) takes columns c0 + 32 wn ..
 //              +31 of both, so g and u of an output meet in one lane.
 // Requires N % 128 == 0 (EPI_F32) or N % 64 == 0 (EPI_SWIGLU), K % 64 == 0.
+// Split K (EPI_F32): workgroup z covers K elements z*kc .. z*kc + kc - 1
+// (kc % 64 == 0) and writes its partial sums to out + z*M*N.
 // ---------------------------------------------------------------------------
 constexpr int kBfTileLine = 128;            // bytes of a row's K step (64 bf16)
 constexpr int kBfTileBuf = 128 * kBfTileLine;
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ W,
                                                            const uint16_t* __restrict__ W3,
                                                            void* __restrict__ out, int64_t M, int N,
-                                                           int K, float limit) {
+                                                           int K, int kc, float limit) {
   __shared__ __attribute__((aligned(1024))) uint8_t As[2][kBfTileBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kBfTileBuf];
   const int tid = threadIdx.x;
@@ -400,6 +402,9 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
   }
   const int64_t xr = m0 + sr < M ? m0 + sr : M - 1;   // rows past M repeat row M-1 (dropped)
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(X) + (size_t)xr * row_bytes;
+  const size_t kofs = (size_t)blockIdx.z * kc * 2;    // this split's first K byte
+  wsrc += kofs;
+  xsrc += kofs;
   uint32_t soff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) soff[j] = sr * kBfTileLine + 16 * ((4 * sh + j) ^ (sr & 7));
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = K / 64;
+  const int steps = kc / 64;
   gload(0);
   lstore(0);
   for (int s = 0; s < steps; ++s) {
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
     const int64_t r = m0 + 64 * wm + 16 * m + col;
     if (r >= M) continue;
     if (EPI == EPI_F32) {
-      float* o = static_cast<float*>(out) + (size_t)r * N;
+      float* o = static_cast<float*>(out) + (size_t)blockIdx.z * M * N + (size_t)r * N;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int c = nb * 128 + 64 * wn + 16 * t + 4 * grp;
@@ -506,7 +511,7 @@ static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16
   if (M <= 64 && K % 1024 == 0) return launch_skinny<EPI>(X, W, W3, out, (int)M, N, K, limit, st);
   if (M >= kBfTileMinM && K % 64 == 0 && N % (EPI == EPI_SWIGLU ? 64 : 128) == 0) {
     const dim3 grid((unsigned)(N / (EPI == EPI_SWIGLU ? 64 : 128)), (unsigned)((M + 127) / 128));
-    hipLaunchKernelGGL((bf16_tile_kernel<EPI>), grid, dim3(256), 0, st, X, W, W3, out, M, N, K,
+    hipLaunchKernelGGL((bf16_tile_kernel<EPI>), grid, dim3(256), 0, st, X, W, W3, out, M, N, K, K,
                        limit);
     return hipGetLastError();
   }
@@ -525,6 +530,26 @@ static hipError_t launch_bf16(const uint16_t* X, const uint16_t* W, const uint16
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
                               int H, int E, hipStream_t st) {
   return launch_bf16<EPI_F32, 1>(x, wg, nullptr, logits, T, E, H, 0.f, st);
+}
+
+// Large batches: the tile kernel has only (E / 128) x (T / 128) workgroups
+// (64 for T = 4096, E = 256), so the K loop is split until about 512
+// workgroups run; the partial sums are added in split order by the top-k
+// kernel.
+int router_tile_splits(int64_t T, int H, int E) {
+  if (T < kBfTileMinM || H % 64 || E % 128) return 1;
+  const int64_t base = (int64_t)(E / 128) * ((T + 127) / 128);
+  int ks = 1;
+  while (ks < 8 && base * ks < 512 && H % (2 * ks * 64) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_tile_split(const uint16_t* x, const uint16_t* wg, float* partial,
+                                    int64_t T, int H, int E, int splits, hipStream_t st) {
+  const dim3 grid((unsigned)(E / 128), (unsigned)((T + 127) / 128), (unsigned)splits);
+  hipLaunchKernelGGL((bf16_tile_kernel<EPI_F32>), grid, dim3(256), 0, st, x, wg, nullptr, partial,
+                     T, E, H, H / splits, 0.f);
+  return hipGetLastError();
 }
 
 int router_splits(int64_t T, int H) {

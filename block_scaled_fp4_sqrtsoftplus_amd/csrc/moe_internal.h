@@ -76,6 +76,12 @@ constexpr int kRouterSplits = 8;
 int router_splits(int64_t T, int H);
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
                                  int H, int E, hipStream_t st);
+// Large batches (T >= 256, H % 64 == 0, E % 128 == 0): the bf16 tile GEMM
+// with K split router_tile_splits(T, H, E) ways (1 = no split), partial sums
+// partial[ks][t][e].
+int router_tile_splits(int64_t T, int H, int E);
+hipError_t launch_router_tile_split(const uint16_t* x, const uint16_t* wg, float* partial,
+                                    int64_t T, int H, int E, int splits, hipStream_t st);
 
 // Scores + top-k from logits given as `splits` partial sums [splits][T][E]
 // (added in split order); logits_out (or NULL) receives their sum.
@@ -87,11 +93,12 @@ hipError_t launch_hash_route(const int64_t* token_ids, int64_t T, int E, int k,
                              float route_scale, uint64_t seed, int32_t* topk_idx, float* topk_w,
                              hipStream_t st);
 
-// Stable counting sort of the P = T*k pairs by expert.
+// Stable counting sort of the P = T*k pairs by expert; with mtile_off (may
+// be null) also the m-tile prefix for tiles of bm pairs.
 size_t permute_scratch_bytes(int64_t P, int E);
 hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* expert_offsets,
-                          int32_t* sorted_pairs, int32_t* pair_pos, void* scratch,
-                          hipStream_t st);
+                          int32_t* sorted_pairs, int32_t* pair_pos, void* scratch, int bm,
+                          int32_t* mtile_off, hipStream_t st);
 
 // Permutation + m-tile prefix (tiles of bm pairs) of a small batch
 // (P <= kFusedMaxPairs, E <= 512) in one workgroup.

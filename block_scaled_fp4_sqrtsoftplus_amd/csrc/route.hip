@@ -183,7 +183,7 @@ __device__ __forceinline__ uint64_t lanes_with_same(int v) {
   }
   return same;
 }
-constexpr int kPermChunk = 1024;  // pairs per chunk (one wave walks 16 rounds of 64)
+constexpr int kPermChunk = 1024;  // pairs per chunk (16 waves of 64)
 
 size_t permute_scratch_bytes(int64_t P, int E) {
   const int64_t chunks = (P + kPermChunk - 1) / kPermChunk;
@@ -204,76 +204,102 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += 256) counts[c * E + e] = h[e];
 }
 
+// inclusive scan of one value per thread over a 512-thread workgroup
+// (Hillis-Steele in LDS)
+__device__ __forceinline__ int32_t block_scan512(int32_t* tot, int32_t v) {
+  const int e = threadIdx.x;
+  tot[e] = v;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    const int32_t u = e >= off ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += u;
+    __syncthreads();
+  }
+  const int32_t r = tot[e];
+  __syncthreads();
+  return r;
+}
+
 // One workgroup: expert totals, exclusive scan -> expert_offsets, then each
-// chunk's base per expert, written over the counts (expert-major order).
+// chunk's base per expert, written over the counts (expert-major order);
+// with mtile_off, also the grouped GEMMs' m-tile prefix for tiles of bm.
 __global__ __launch_bounds__(512) void perm_scan_kernel(int32_t* __restrict__ counts, int chunks,
-                                                        int E, int32_t* __restrict__ offsets) {
+                                                        int E, int32_t* __restrict__ offsets,
+                                                        int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int32_t tot[512];
   const int e = threadIdx.x;
   int32_t sum = 0;
   if (e < E)
     for (int c = 0; c < chunks; ++c) sum += counts[(size_t)c * E + e];
-  tot[e] = sum;
-  __syncthreads();
-  // inclusive scan over experts (Hillis-Steele, 512 entries)
-  for (int off = 1; off < 512; off <<= 1) {
-    const int32_t v = e >= off ? tot[e - off] : 0;
-    __syncthreads();
-    tot[e] += v;
-    __syncthreads();
-  }
+  const int32_t incl = block_scan512(tot, sum);
   if (e < E) {
-    int32_t base = tot[e] - sum;  // exclusive
+    int32_t base = incl - sum;  // exclusive
     offsets[e] = base;
-    if (e == E - 1) offsets[E] = tot[e];
+    if (e == E - 1) offsets[E] = incl;
     for (int c = 0; c < chunks; ++c) {
       const int32_t n = counts[(size_t)c * E + e];
       counts[(size_t)c * E + e] = base;
       base += n;
     }
   }
+  if (mtile_off) {
+    const int32_t t = e < E ? (sum + bm - 1) / bm : 0;
+    const int32_t ti = block_scan512(tot, t);
+    if (e < E) {
+      mtile_off[e] = ti - t;
+      if (e == E - 1) mtile_off[E] = ti;
+    }
+  }
 }
 
-// One wave per chunk: walk the chunk 64 pairs at a time in order; a lane's
-// position is its expert's running base plus the number of lower lanes with
-// the same expert in this round.
-__global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t* __restrict__ idx,
-                                                          int64_t P, int E,
-                                                          const int32_t* __restrict__ base,
-                                                          int32_t* __restrict__ sorted_pairs,
-                                                          int32_t* __restrict__ pair_pos) {
-  __shared__ int32_t run[512];
+// One workgroup of 16 waves per chunk; wave w ranks the w-th 64 pairs of the
+// chunk.  A pair's position is its expert's base for the chunk, plus the
+// counts of its expert in the chunk's lower waves (per-wave counts in LDS,
+// summed per expert over the waves), plus the number of lower lanes of its
+// wave with the same expert -- the stable order, with all 16 rounds of 64
+// in flight at once.
+__global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __restrict__ idx,
+                                                            int64_t P, int E,
+                                                            const int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ sorted_pairs,
+                                                            int32_t* __restrict__ pair_pos) {
+  constexpr int W = kPermChunk / 64;
+  __shared__ int32_t cnt[W][512];
   const int64_t c = blockIdx.x;
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = base[c * E + e];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < W * 512; i += 1024) (&cnt[0][0])[i] = 0;
+  const int64_t p = c * kPermChunk + (int64_t)w * 64 + lane;
+  const bool live = p < P;
+  const int ex = live ? idx[p] : -1;
+  const uint64_t same = lanes_with_same(ex);
+  const int rank = __popcll(same & ((1ull << lane) - 1ull));
   __syncthreads();
-  const int64_t lo = c * kPermChunk;
-  const int64_t hi = min(P, lo + kPermChunk);
-  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
-    const int64_t p = r0 + lane;
-    const bool live = p < hi;
-    const int ex = live ? idx[p] : -1;
-    // lanes with the same expert
-    const uint64_t same = lanes_with_same(ex);
-    const uint64_t lower = same & ((1ull << lane) - 1ull);
-    const int rank = __popcll(lower);
-    const int cnt = __popcll(same);
-    int32_t pos = 0;
-    if (live) pos = run[ex] + rank;
-    __syncthreads();
-    if (live) {
-      sorted_pairs[pos] = (int32_t)p;
-      pair_pos[p] = pos;
-      // the highest lane of each expert advances that expert's running base
-      if ((same >> lane) == 1ull) run[ex] += cnt;
+  // the highest lane of each expert's group in this wave records the count
+  if (live && (same >> lane) == 1ull) cnt[w][ex] = __popcll(same);
+  __syncthreads();
+  // exclusive running sum over the waves, per expert, from the chunk's base
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int32_t run = base[c * E + e];
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const int32_t n = cnt[v][e];
+      cnt[v][e] = run;
+      run += n;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (live) {
+    const int32_t pos = cnt[w][ex] + rank;
+    sorted_pairs[pos] = (int32_t)p;
+    pair_pos[p] = pos;
   }
 }
 
 hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* expert_offsets,
-                          int32_t* sorted_pairs, int32_t* pair_pos, void* scratch,
-                          hipStream_t st) {
+                          int32_t* sorted_pairs, int32_t* pair_pos, void* scratch, int bm,
+                          int32_t* mtile_off, hipStream_t st) {
   const int64_t chunks = (P + kPermChunk - 1) / kPermChunk;
   int32_t* counts = static_cast<int32_t*>(scratch);
   if (chunks > 0) {
@@ -281,10 +307,10 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* ex
                        counts);
   }
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(512), 0, st, counts, (int)chunks, E,
-                     expert_offsets);
+                     expert_offsets, bm, mtile_off);
   if (chunks > 0) {
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)chunks), dim3(64), 0, st, topk_idx, P,
-                       E, counts, sorted_pairs, pair_pos);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)chunks), dim3(1024), 0, st, topk_idx,
+                       P, E, counts, sorted_pairs, pair_pos);
   }
   return hipGetLastError();
 }
