@@ -60,6 +60,31 @@ __device__ __forceinline__ v4f mfma_w4(const v8i& a, const v8i& b, int sa, int s
   return d;
 }
 
+// Twelve MFMAs from zero: for the four activation operands a[m] (block
+// scales sa[m]), c[m] = a[m] . eights, d0[m] = a[m] . b0, d1[m] = a[m] . b1;
+// one 2-wait-state lead and one 32-wait-state guard for the group, so the
+// matrix pipe gets all twelve back to back.
+__device__ __forceinline__ void mfma_w4x12(const v8i (&a)[4], const v8i& eights, const v8i& b0,
+                                           const v8i& b1, const int (&sa)[4], int sb,
+                                           v4f (&c)[4], v4f (&d0)[4], v4f (&d1)[4]) {
+#define W4X12_ROW(M)                                                                      \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[c" #M "], %[a" #M "], %[e], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[x" #M "], %[a" #M "], %[b0], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[y" #M "], %[a" #M "], %[b1], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t"
+  asm volatile(
+      "s_nop 1\n\t"
+      W4X12_ROW(0) W4X12_ROW(1) W4X12_ROW(2) W4X12_ROW(3)
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]),
+        [x0] "=&v"(d0[0]), [x1] "=&v"(d0[1]), [x2] "=&v"(d0[2]), [x3] "=&v"(d0[3]),
+        [y0] "=&v"(d1[0]), [y1] "=&v"(d1[1]), [y2] "=&v"(d1[2]), [y3] "=&v"(d1[3])
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [e] "v"(eights),
+        [b0] "v"(b0), [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]),
+        [s3] "v"(sa[3]), [t] "v"(sb));
+#undef W4X12_ROW
+}
+
 // 32 INT4 codes (16 bytes of a weight row) -> the E4M3 bytes q + 8 of the
 // B operand: dword 2i holds elements 8i, 8i+2, 8i+4, 8i+6, dword 2i+1 the
 // odd ones 8i+1 .. 8i+7
@@ -85,7 +110,8 @@ __device__ __forceinline__ v8i act_operand(const v4u& b0, const v4u& b1) {
 }
 
 __device__ __forceinline__ bool map_tile_w4(const ExpertGemmArgs& p, int mt_max, int n_tiles,
-                                            int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
+                                            int bm, int& n_tile, int& e, int& m0, int& off_e,
+                                            int& n_e) {
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int w = (b & 7) * (G >> 3) + (b >> 3);   // XCD-aware: consecutive ids per XCD
@@ -99,7 +125,7 @@ __device__ __forceinline__ bool map_tile_w4(const ExpertGemmArgs& p, int mt_max,
     if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
   }
   e = lo;
-  m0 = (mt - p.mtile_off[e]) * 16;
+  m0 = (mt - p.mtile_off[e]) * bm;
   off_e = p.expert_offsets[e];
   n_e = p.expert_offsets[e + 1] - off_e;
   return true;
@@ -120,7 +146,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
                                                                    int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_w4(p, mt_max, n_tiles, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_tile_w4(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -306,15 +332,245 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Larger batches: m-tiles of 64 pairs (K <= 4096)
+// ---------------------------------------------------------------------------
+// Eight waves of 32 weight rows (GEMM1: 16 h columns, their w1 and w3 rows;
+// GEMM2: 32 output columns), the register ring of weight steps as above.
+// The m-tile's 64 activation rows of a K step are staged once in LDS (double
+// buffer; 16-byte chunks xor-swizzled by row, so that the 16 rows a wave
+// reads at one offset hit distinct banks) and every wave takes four 16-pair
+// sub-tiles from there: each unpacked weight operand feeds four MFMAs.  The
+// waves' float32 scale lines (rows padded to 33) and the 64 tokens'
+// activation scales stay in LDS for the whole tile; one barrier per K step.
+constexpr int kW4M = 64;
+constexpr int kW4MThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmArgs p,
+                                                                      int mt_max, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t xl[2][kW4M * 128];
+  __shared__ float wsl[8][32][33];
+  __shared__ __attribute__((aligned(16))) uint8_t bsl[kW4M][32];
+  __shared__ float red[8][kW4M];
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile_w4(p, mt_max, n_tiles, kW4M, n_tile, e, m0, off_e, n_e)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int S = K / 128;                    // a multiple of 4, at most 32
+  const size_t wrow_bytes = (size_t)K / 2;
+
+  const uint8_t* wptr[2];
+  const float* srow[2];
+  int n0;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+    const int row = n0 + 16 * wv + col;       // h column: its w1 row (t 0) and w3 row (t 1)
+    wptr[0] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+    wptr[1] = p.w3 + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+    srow[0] = reinterpret_cast<const float*>(p.w_scale) + ((size_t)e * N + row) * S;
+    srow[1] = reinterpret_cast<const float*>(p.w3_scale) + ((size_t)e * N + row) * S;
+  } else {
+    n0 = n_tile * kG2Rows;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = min(n0 + 32 * wv + 16 * t + col, N - 1);
+      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      srow[t] = reinterpret_cast<const float*>(p.w_scale) + ((size_t)e * N + row) * S;
+    }
+  }
+
+  // staging role: thread (sr, sq) moves the 16-byte chunk sq of token row sr
+  // of each step; rows past the expert's last pair repeat that pair's row
+  // (computed, dropped)
+  const int sr = threadIdx.x >> 3, sq = threadIdx.x & 7;
+  const int sslot = min(m0 + sr, n_e - 1);
+  const int64_t stok = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + sslot] / p.top_k)
+                                   : (int64_t)(off_e + sslot);
+  const uint8_t* xsrc = p.a + stok * K + 16 * sq;
+  const int xc = sr * 128 + (sq ^ (sr & 7)) * 16;
+
+  // tile-long LDS tables: the 64 tokens' activation scales and this wave's
+  // weight scale lines (positions past S clamp to S - 4: same data)
+  {
+    const int b0 = min(4 * sq, S - 4);
+    *reinterpret_cast<uint32_t*>(&bsl[sr][b0]) =
+        *reinterpret_cast<const uint32_t*>(p.a_scale + stok * S + b0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int f0 = min(8 * grp, S - 4), f1 = min(8 * grp + 4, S - 4);
+      const v4u a0 = *reinterpret_cast<const v4u*>(srow[t] + f0);
+      const v4u a1 = *reinterpret_cast<const v4u*>(srow[t] + f1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wsl[wv][16 * t + col][f0 + j] = __uint_as_float(a0[j]);
+        wsl[wv][16 * t + col][f1 + j] = __uint_as_float(a1[j]);
+      }
+    }
+  }
+
+  v4f acc[2][4];   // [weight tile][16-pair sub-tile]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
+                      0x08080808, 0x08080808, 0x08080808, 0x08080808};
+  v4u A[4][2];     // weight ring: [step][tile]
+  v4u R;           // the chunk of the next step to stage
+  auto load_w = [&](int s, v4u (&a)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
+  };
+  auto load_x = [&](int s) { R = *reinterpret_cast<const v4u*>(xsrc + (size_t)s * 128); };
+  auto store_x = [&](int buf) { *reinterpret_cast<v4u*>(&xl[buf][xc]) = R; };
+
+  // one K step from the weight ring slot a and LDS buffer buf
+  auto compute = [&](int s, const v4u (&a)[2], int buf) {
+    const v8i b0 = int4_operand(a[0]), b1 = int4_operand(a[1]);
+    const float sw0 = wsl[wv][col][s], sw1 = wsl[wv][16 + col][s];
+    v8i xa[4];
+    int sa[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* xr = &xl[buf][(16 * m + col) * 128];
+      const v4u lo = *reinterpret_cast<const v4u*>(xr + ((2 * grp) ^ (col & 7)) * 16);
+      const v4u hi = *reinterpret_cast<const v4u*>(xr + ((2 * grp + 1) ^ (col & 7)) * 16);
+      xa[m] = act_operand(lo, hi);
+      sa[m] = bsl[16 * m + col][s];
+    }
+    v4f c[4], d0[4], d1[4];
+    mfma_w4x12(xa, eights, b0, b1, sa, kW4ScaleB, c, d0, d1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        acc[0][m][v] = __builtin_fmaf(d0[m][v] - c[m][v], sw0, acc[0][m][v]);
+        acc[1][m][v] = __builtin_fmaf(d1[m][v] - c[m][v], sw1, acc[1][m][v]);
+      }
+  };
+  // one group of four steps; LOAD: refill the weight ring with the next group
+  // (two steps at a time: both halves of each 128-byte line back to back)
+  auto group = [&](int s0, auto load) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int s = s0 + d;
+      compute(s, A[d], s & 1);
+      store_x((s + 1) & 1);                 // step s + 1 (the last step's copy is unused)
+      load_x(min(s + 2, S - 1));
+      if constexpr (decltype(load)::value) {
+        if (d & 1) {
+          load_w(s0 + 3 + d, A[d - 1]);
+          load_w(s0 + 4 + d, A[d]);
+        }
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);   // no work moved across steps
+    }
+  };
+
+  load_x(0);
+  store_x(0);
+  load_x(min(1, S - 1));
+#pragma unroll
+  for (int d = 0; d < 4; ++d) load_w(d, A[d]);
+  __syncthreads();
+  for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
+  group(S - 4, std::false_type{});
+
+  // lane holds acc[t][m][v] = output (token 16 m + 4 grp + v, weight row col
+  // of tile t)
+  if (MODE == 1) {
+    const float lim = p.limit;
+    float h[4][4];
+    float amax[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = fminf(fmaxf(acc[0][m][v], -lim), lim);
+        const float u = fminf(fmaxf(acc[1][m][v], -lim), lim);
+        h[m][v] = silu_w4(g) * u;
+        float a = fabsf(h[m][v]);
+#pragma unroll
+        for (int k = 1; k < 16; k <<= 1) a = fmaxf(a, __shfl_xor(a, k));
+        amax[m][v] = a;
+      }
+    if (col == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wv][16 * m + 4 * grp + v] = amax[m][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = 16 * m + 4 * grp + v;
+        if (m0 + tok >= n_e) continue;
+        float bmax = red[0][tok];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) bmax = fmaxf(bmax, red[w][tok]);
+        const int ex = pow2_scale_exp(bmax);
+        const size_t row = (size_t)(off_e + m0 + tok);
+        p.hq[row * N + n0 + 16 * wv + col] = (uint8_t)e4m3_rne(ldexpf(h[m][v], -ex));
+        if (wv == 0 && col == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+      }
+  } else {
+    if (n0 + 32 * wv >= N) return;
+    // the output addresses are formed only now (an opaque copy of the row
+    // base keeps the compiler from computing them before the K loop and
+    // holding them through it)
+    int rbase = off_e + m0;
+    asm volatile("" : "+s"(rbase));
+    const size_t c0 = (size_t)n0 + 32 * wv + col;   // + 16 t
+    if (p.out_fp32) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = 16 * m + 4 * grp + v;
+          if (m0 + tok >= n_e) continue;
+          float* o = reinterpret_cast<float*>(p.out) + (size_t)(rbase + tok) * N + c0;
+          o[0] = acc[0][m][v];
+          o[16] = acc[1][m][v];
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = 16 * m + 4 * grp + v;
+          if (m0 + tok >= n_e) continue;
+          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (size_t)(rbase + tok) * N + c0;
+          o[0] = (uint16_t)f32_to_bf16(acc[0][m][v]);
+          o[16] = (uint16_t)f32_to_bf16(acc[1][m][v]);
+        }
+    }
+  }
+}
+
 static unsigned pad8_w4(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
 
 template <int MODE>
-static hipError_t launch_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
+static hipError_t launch_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
   if (a.K % 512) return hipErrorInvalidValue;
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8_w4((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (a.K <= 4096)
+  if (bm == kW4M) {
+    if (a.K > 4096) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((expert_gemm_w4_m64<MODE>), dim3(grid), dim3(kW4MThreads), 0, st, a,
+                       mt_max, n_tiles);
+  } else if (bm != 16) {
+    return hipErrorInvalidValue;
+  } else if (a.K <= 4096)
     hipLaunchKernelGGL((expert_gemm_w4<MODE, true>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   else
@@ -323,11 +579,11 @@ static hipError_t launch_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st)
   return hipGetLastError();
 }
 
-hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
-  return launch_w4<1>(a, mt_max, st);
+hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
+  return launch_w4<1>(a, bm, mt_max, st);
 }
-hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
-  return launch_w4<2>(a, mt_max, st);
+hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
+  return launch_w4<2>(a, bm, mt_max, st);
 }
 
 }  // namespace moe

@@ -138,9 +138,10 @@ hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipS
 // NVFP4 weights (E4M3 scale per 16), m-tiles of 16 pairs, K % 512 == 0.
 hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
-// W4AFP8 weights (INT4 + float32 scale per 128), m-tiles of 16 pairs, K % 512 == 0.
-hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
-hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
+// W4AFP8 weights (INT4 + float32 scale per 128), K % 512 == 0; m-tiles of
+// bm = 16 pairs, or 64 when K <= 4096.
+hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+hipError_t launch_expert_gemm2_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 
 // MXFP4 [rows, K/2] + [rows, K/32] -> FP8 E4M3 [rows, K] + E8M0 [rows, K/128].
 hipError_t launch_cast_fp8(const uint8_t* w, const uint8_t* ws, uint8_t* q, uint8_t* qs,
