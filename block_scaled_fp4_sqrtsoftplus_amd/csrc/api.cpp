@@ -222,7 +222,8 @@ int choose_bm(const moe_config& c) {
 moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t* wg,
                          const float* bias, const int64_t* ids, const float* logits_in,
                          float* logits_out, const moe_routing& r, const RouteWs& ws,
-                         hipStream_t st, int32_t* mtile_off = nullptr, bool* tiles_done = nullptr) {
+                         hipStream_t st, int32_t* mtile_off = nullptr, bool* tiles_done = nullptr,
+                         uint8_t* xq = nullptr, uint8_t* xs = nullptr) {
   const int64_t T = c.tokens, P = T * c.top_k;
   if (tiles_done) *tiles_done = false;
   if (c.route_mode == MOE_ROUTE_HASH) {
@@ -237,7 +238,7 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
     MOE_TRY(launch_score_topk(ws.logits, ks, logits_out, bias, T, c.n_experts, c.top_k,
                               c.route_scale, r.topk_idx, r.topk_w, st));
   } else if (router_splits(T, c.hidden) > 1) {
-    MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, st));
+    MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, xq, xs, st));
     MOE_TRY(launch_score_topk(ws.logits, router_splits(T, c.hidden), logits_out, bias, T,
                               c.n_experts, c.top_k, c.route_scale, r.topk_idx, r.topk_w, st));
   } else {
@@ -494,10 +495,14 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   };
   const bool early_fork = shared && c.tokens >= kEarlyForkTokens;
   if (early_fork && (s = fork_shared()) != MOE_OK) return s;
-  MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
+  // small score-routed batches quantize x inside the split-K router launch
+  const bool quant_in_router =
+      c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && router_splits(c.tokens, c.hidden) > 1;
+  if (!quant_in_router) MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
   bool tiles_done = false;
   if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
-                         l.ffn.mtile_off, &tiles_done)) != MOE_OK)
+                         l.ffn.mtile_off, &tiles_done, quant_in_router ? l.xq : nullptr,
+                         quant_in_router ? l.xs : nullptr)) != MOE_OK)
     return s;
   if (shared && !early_fork && (s = fork_shared()) != MOE_OK) return s;
   if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,

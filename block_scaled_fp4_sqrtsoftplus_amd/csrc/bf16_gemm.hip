@@ -290,13 +290,17 @@ static hipError_t launch_skinny(const uint16_t* X, const uint16_t* W, const uint
 // [ks K/KS, (ks+1) K/KS); each wave loads its 1/8 of that slice in one go
 // (no loop), the 8 partial sums meet in a fixed-order LDS tree, and the
 // workgroup writes partial[ks][t][e].  The top-k kernel adds the KS partials
-// in ks order, so the logits do not depend on timing.
+// in ks order, so the logits do not depend on timing.  With q, the same
+// workgroups also quantize x to FP8 (the layer's next step, which reads the
+// same rows): 32 blocks of 128 per workgroup and pass, one launch fewer.
 // ---------------------------------------------------------------------------
 template <int MT, int STEPS>
 __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ W,
                                                             float* __restrict__ partial, int M,
-                                                            int N, int K, int KS) {
+                                                            int N, int K, int KS,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ qscale) {
   constexpr int NACC = MT * 4;
   __shared__ float red[4][NACC][64];
   const int lane = threadIdx.x & 63;
@@ -305,6 +309,13 @@ __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __re
   const int grp = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int ks = blockIdx.y;
+  if (q) {
+    const int64_t n_blocks = (int64_t)M * (K / 128);
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * 32;
+    for (int64_t b = ((int64_t)ks * gridDim.x + blockIdx.x) * 32 + (threadIdx.x >> 4); b < n_blocks;
+         b += stride)
+      quant_act_block(X, b, n_blocks, threadIdx.x & 15, q, qscale);
+  }
   const int k0 = ks * (K / KS) + wv * STEPS * 32;
   const uint16_t* wp = W + (size_t)min(n0 + col, N - 1) * K + k0 + 8 * grp;
   uint4 A[STEPS], B[STEPS][MT];
@@ -561,13 +572,14 @@ int router_splits(int64_t T, int H) {
 }
 
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
-                                 int H, int E, hipStream_t st) {
+                                 int H, int E, uint8_t* q, uint8_t* scale, hipStream_t st) {
   const int KS = kRouterSplits;
   const int steps = H / KS / 8 / 32;   // per wave
   const dim3 grid((unsigned)((E + 15) / 16), (unsigned)KS);
   const int M = (int)T;
 #define MOE_ROUTER_LAUNCH(MT, ST) \
-  hipLaunchKernelGGL((router_splitk_kernel<MT, ST>), grid, dim3(512), 0, st, x, wg, partial, M, E, H, KS)
+  hipLaunchKernelGGL((router_splitk_kernel<MT, ST>), grid, dim3(512), 0, st, x, wg, partial, M, E, H, KS, \
+                     q, scale)
   const int mt = (M + 15) / 16;
   if (steps == 2) {
     if (mt == 1) MOE_ROUTER_LAUNCH(1, 2); else if (mt == 2) MOE_ROUTER_LAUNCH(2, 2);

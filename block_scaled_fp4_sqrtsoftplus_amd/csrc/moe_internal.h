@@ -51,6 +51,41 @@ __device__ __forceinline__ uint32_t e4m3_rne(float s) {
   return code | sign;
 }
 
+// FP8 E4M3 quantization of the 128-element block blk of a bf16 array (one
+// power-of-two scale per block, smallest with amax <= 448 * 2^e): 16 lanes
+// (sub = 0..15, consecutive lanes of one wave) take 8 elements each.  Blocks
+// at or past n_blocks compute on zeros and store nothing.
+__device__ __forceinline__ void quant_act_block(const uint16_t* __restrict__ x, int64_t blk,
+                                                int64_t n_blocks, int sub, uint8_t* __restrict__ q,
+                                                uint8_t* __restrict__ scale) {
+  const bool live = blk < n_blocks;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4*>(x + blk * 128 + sub * 8);
+  float v[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // reduce over the 16 lanes of the block (xor partners stay inside the group)
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = pow2_scale_exp(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_rne(ldexpf(v[i], -e)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_rne(ldexpf(v[4 + i], -e)) << (8 * i);
+  if (live) {
+    *reinterpret_cast<uint2*>(q + blk * 128 + sub * 8) = make_uint2(lo, hi);
+    if (sub == 0) scale[blk] = (uint8_t)(e + 127);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiling constants of the grouped expert GEMMs
 // ---------------------------------------------------------------------------
@@ -74,8 +109,10 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logi
 // and H a multiple of kRouterSplits * 512), else it returns 1.
 constexpr int kRouterSplits = 8;
 int router_splits(int64_t T, int H);
+// With q (may be null) the same launch also quantizes x to q / scale (as
+// launch_quant_act).
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
-                                 int H, int E, hipStream_t st);
+                                 int H, int E, uint8_t* q, uint8_t* scale, hipStream_t st);
 // Large batches (T >= 256, H % 64 == 0, E % 128 == 0): the bf16 tile GEMM
 // with K split router_tile_splits(T, H, E) ways (1 = no split), partial sums
 // partial[ks][t][e].

@@ -2,12 +2,13 @@
 // of the routed experts per token, sqrtsoftplus scores, hash routing in the
 // first layers, routing scale 1.5).
 //
-//  score_topk  one wave per token; lane l owns experts l, l+64, ...; the score
-//              s = sqrt(ln(1 + e^z)) is evaluated in double and rounded to fp32;
-//              key = s + bias; k rounds of a wave arg-max (larger key first,
-//              lower expert id on equal keys) built from two DPP wave
-//              reductions each; weights s_j / sum(s) * scale in fp32 with the
-//              sum taken in rank order (IEEE division).
+//  score_topk  one workgroup of 4 waves per token; thread i owns experts i,
+//              i + 256; the score s = sqrt(ln(1 + e^z)) is evaluated in double
+//              and rounded to fp32; key = s + bias; k rounds of a wave arg-max
+//              (larger key first, lower expert id on equal keys) built from two
+//              DPP wave reductions each, per wave and then over the waves'
+//              candidates; weights s_j / sum(s) * scale in fp32 with the sum
+//              taken in rank order (IEEE division).
 //  hash_route  one thread per token: SplitMix64 (Steele, Lea, Flood, OOPSLA
 //              2014) from (seed << 32) ^ token_id; r mod E with r at or above
 //              2^64 - (2^64 mod E) rejected, repeats skipped, first k kept.
@@ -19,8 +20,6 @@
 #include "moe_internal.h"
 
 namespace moe {
-
-constexpr int kMaxExpertsPerLane = 8;  // E <= 512
 
 extern "C" __device__ unsigned int __ockl_wfred_max_u32(unsigned int);
 extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
@@ -34,6 +33,11 @@ __device__ __forceinline__ uint32_t key_order(float k) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One 256-thread workgroup per token: thread i owns experts i and i + 256,
+// so each lane evaluates at most two scores (the double-precision chain is
+// the kernel's latency); each wave selects its own top k, and wave 0 selects
+// the token's top k from the 4k candidates -- the same order, since the
+// token's top k is among the union of the waves' top k.
 __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict__ logits,
                                                          int splits, float* __restrict__ logits_out,
                                                          const float* __restrict__ bias,
@@ -41,29 +45,32 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
                                                          float route_scale,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w) {
+  __shared__ uint32_t cand_key[4][8];
+  __shared__ int32_t cand_e[4][8];
+  __shared__ float cand_s[4][8];
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int wv = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
   const float* z = logits + t * E;
   const size_t split_stride = (size_t)T * E;
-  float s[kMaxExpertsPerLane];
-  uint32_t ok[kMaxExpertsPerLane];
+  float s[2];
+  uint32_t ok[2];
 #pragma unroll
-  for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-    const int ex = lane + 64 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int ex = (int)threadIdx.x + 256 * i;
     if (ex < E) {
       float zf;
       if (splits == kRouterSplits) {
         // all partial loads in flight first, then the fixed-order sum
         float part[kRouterSplits];
 #pragma unroll
-        for (int p = 0; p < kRouterSplits; ++p) part[p] = z[p * split_stride + ex];
+        for (int q = 0; q < kRouterSplits; ++q) part[q] = z[q * split_stride + ex];
         zf = part[0];
 #pragma unroll
-        for (int p = 1; p < kRouterSplits; ++p) zf += part[p];
+        for (int q = 1; q < kRouterSplits; ++q) zf += part[q];
       } else {
         zf = z[ex];
-        for (int p = 1; p < splits; ++p) zf += z[p * split_stride + ex];
+        for (int q = 1; q < splits; ++q) zf += z[q * split_stride + ex];
       }
       if (logits_out) logits_out[t * E + ex] = zf;
       const double zd = (double)zf;
@@ -74,31 +81,44 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
       ok[i] = 0u;
     }
   }
+  // this wave's top k: k rounds of a wave arg-max (largest key, then the
+  // lowest expert id), the winner retired by its owner
+  for (int j = 0; j < k; ++j) {
+    const int i = ok[1] > ok[0] ? 1 : 0;          // equal keys: the lower id (slot 0)
+    const uint32_t bk = ok[i];
+    const uint32_t be = bk ? (uint32_t)(threadIdx.x + 256 * i) : 0xFFFFFFFFu;
+    const uint32_t m = __ockl_wfred_max_u32(bk);
+    const uint32_t win = __ockl_wfred_min_u32(bk == m ? be : 0xFFFFFFFFu);
+    const int wl = (int)(win & 63);               // owner lane: win = 64 wv + wl (+ 256)
+    float ws = 0.f;
+    if (m != 0u) {
+      ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(win >= 256 ? s[1] : s[0]), wl));
+      if (lane == wl) ok[win >= 256 ? 1 : 0] = 0u;
+    }
+    if (lane == 0) {
+      cand_key[wv][j] = m;
+      cand_e[wv][j] = m ? (int32_t)win : 0x7FFFFFFF;
+      cand_s[wv][j] = ws;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // the token's top k among the 4k candidates (lane l < 4k holds one)
+  const bool has = lane < 4 * k;
+  uint32_t ck = has ? cand_key[lane / k][lane % k] : 0u;
+  const int32_t ce = has ? cand_e[lane / k][lane % k] : 0x7FFFFFFF;
+  const float cs = has ? cand_s[lane / k][lane % k] : 0.f;
   int sel_e[8];
   float sel_s[8];
   for (int j = 0; j < k; ++j) {
-    // lane-local best: largest key, lower expert id on equal keys (slots are
-    // visited in ascending expert order, so '>' keeps the lower id)
-    uint32_t bk = 0u;
-    uint32_t be = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i)
-      if (ok[i] > bk) { bk = ok[i]; be = (uint32_t)(lane + 64 * i); }
-    // wave arg-max in two DPP reductions: the largest key, then the lowest
-    // expert id among the lanes holding it
-    const uint32_t m = __ockl_wfred_max_u32(bk);
-    const int win = (int)__ockl_wfred_min_u32(bk == m ? be : 0xFFFFFFFFu);
+    const uint32_t m = __ockl_wfred_max_u32(ck);
+    const int win = (int)__ockl_wfred_min_u32(ck == m ? (uint32_t)ce : 0xFFFFFFFFu);
     sel_e[j] = win;
-    // the owner lane retires the winner; its unbiased score is broadcast
-    const int wl = win & 63, wi = win >> 6;
-    float ws = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i)
-      if (i == wi) {
-        ws = s[i];
-        if (lane == wl) ok[i] = 0u;
-      }
-    sel_s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
+    // the lane holding the winner (unique: experts are distinct)
+    const uint64_t hold = __ballot(ck == m && ce == win);
+    const int hl = (int)__builtin_ctzll(hold);
+    sel_s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), hl));
+    if (lane == hl) ck = 0u;
   }
   if (lane == 0) {
     float total = 0.f;
@@ -114,8 +134,8 @@ hipError_t launch_score_topk(const float* logits, int splits, float* logits_out,
                              int64_t T, int E, int k, float route_scale, int32_t* topk_idx,
                              float* topk_w, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits,
-                     splits, logits_out, bias, T, E, k, route_scale, topk_idx, topk_w);
+  hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)T), dim3(256), 0, st, logits, splits,
+                     logits_out, bias, T, E, k, route_scale, topk_idx, topk_w);
   return hipGetLastError();
 }
 
