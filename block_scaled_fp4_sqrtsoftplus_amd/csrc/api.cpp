@@ -207,9 +207,8 @@ moe_status check_weights(const moe_expert_weights* w) {
 int choose_bm(const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
   if (P <= (int64_t)32 * c.n_experts) return 16;
-  if (c.expert_format == MOE_EXPERTS_NVFP4) return 16;   // one kernel, 16-pair tiles
-  if (c.expert_format == MOE_EXPERTS_W4AFP8)             // 64-pair tiles need K <= 4096
-    return (c.hidden <= 4096 && c.inter <= 4096) ? 64 : 16;
+  if (c.expert_format == MOE_EXPERTS_NVFP4 || c.expert_format == MOE_EXPERTS_W4AFP8)
+    return (c.hidden <= 4096 && c.inter <= 4096) ? 64 : 16;   // 64-pair tiles need K <= 4096
   if (c.expert_format == MOE_EXPERTS_FP8) return 64;     // no 128-pair FP8 tile kernel
   auto tiled = [](int k) { return k == 1024 || k == 2048 || k == 4096; };
   return (tiled(c.hidden) && tiled(c.inter)) ? 128 : 64;
@@ -290,7 +289,7 @@ moe_status enqueue_ffn(const moe_config& c, const uint8_t* xq, const uint8_t* xs
   a.hq = hq;
   a.hs = hs;
   const int fmt = c.expert_format;
-  MOE_TRY(fmt == MOE_EXPERTS_NVFP4    ? launch_expert_gemm1_nv(a, mt_max, st)
+  MOE_TRY(fmt == MOE_EXPERTS_NVFP4    ? launch_expert_gemm1_nv(a, bm, mt_max, st)
           : fmt == MOE_EXPERTS_W4AFP8 ? launch_expert_gemm1_w4(a, bm, mt_max, st)
                                       : launch_expert_gemm1(a, bm, mt_max, st));
   // GEMM2: hq (FP8) x w2 -> out
@@ -305,7 +304,7 @@ moe_status enqueue_ffn(const moe_config& c, const uint8_t* xq, const uint8_t* xs
   b.N = c.hidden;
   b.out = out;
   b.out_fp32 = out_fp32;
-  MOE_TRY(fmt == MOE_EXPERTS_NVFP4    ? launch_expert_gemm2_nv(b, mt_max, st)
+  MOE_TRY(fmt == MOE_EXPERTS_NVFP4    ? launch_expert_gemm2_nv(b, bm, mt_max, st)
           : fmt == MOE_EXPERTS_W4AFP8 ? launch_expert_gemm2_w4(b, bm, mt_max, st)
                                       : launch_expert_gemm2(b, bm, mt_max, st));
   return MOE_OK;

@@ -56,7 +56,7 @@ __device__ __forceinline__ h8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
 }
 
 __device__ __forceinline__ bool map_tile_nv(const ExpertGemmArgs& p, int mt_max, int n_tiles,
-                                            int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
+                                            int bm, int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int w = (b & 7) * (G >> 3) + (b >> 3);   // XCD-aware: consecutive ids per XCD
@@ -70,7 +70,7 @@ __device__ __forceinline__ bool map_tile_nv(const ExpertGemmArgs& p, int mt_max,
     if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
   }
   e = lo;
-  m0 = (mt - p.mtile_off[e]) * 16;
+  m0 = (mt - p.mtile_off[e]) * bm;
   off_e = p.expert_offsets[e];
   n_e = p.expert_offsets[e + 1] - off_e;
   return true;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
                                                                 int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_nv(p, mt_max, n_tiles, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_tile_nv(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -320,15 +320,242 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Larger batches: m-tiles of 64 pairs (K <= 4096)
+// ---------------------------------------------------------------------------
+// Eight waves of 32 weight rows (GEMM1: 16 h columns, their w1 and w3 rows;
+// GEMM2: 32 output columns); the register ring of weight steps as above.
+// The m-tile's 64 activation rows of a K step are converted to fp16 once,
+// by the staging lanes, into LDS (double buffer; 16-byte chunk c of a row at
+// slot c ^ (row & 15), so that the 16 rows a wave reads at one offset hit
+// distinct banks), and every wave takes four 16-pair sub-tiles from there:
+// each dequantized weight operand feeds four MFMAs.  The waves' scale lines
+// (staged as in the LINE streaming kernel) and the 64 tokens' activation
+// scales stay in LDS for the tile; one barrier per K step.
+constexpr int kNvM = 64;
+constexpr int kNvMThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmArgs p,
+                                                                      int mt_max, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t xl[2][kNvM * 256];   // fp16 activations
+  __shared__ __attribute__((aligned(16))) uint8_t bsl[kNvM][32];
+  __shared__ float red[8][kNvM];
+  int n_tile, e, m0, off_e, n_e;
+  if (!map_tile_nv(p, mt_max, n_tiles, kNvM, n_tile, e, m0, off_e, n_e)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int S = K / 128;                    // a multiple of 4, at most 32
+  const size_t wrow_bytes = (size_t)K / 2;
+  const size_t srow_bytes = (size_t)K / 16;
+
+  const uint8_t* wptr[2];
+  const uint8_t* srow[2];
+  int n0;
+  if (MODE == 1) {
+    n0 = n_tile * kG1Cols;
+    const int row = n0 + 16 * wv + col;       // h column: its w1 row (t 0) and w3 row (t 1)
+    wptr[0] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+    wptr[1] = p.w3 + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+    srow[0] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+    srow[1] = p.w3_scale + ((size_t)e * N + row) * srow_bytes;
+  } else {
+    n0 = n_tile * kG2Rows;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = min(n0 + 32 * wv + 16 * t + col, N - 1);
+      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      srow[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+    }
+  }
+  uint8_t* const lds_sc = reinterpret_cast<uint8_t*>(nv_lds) + wv * (32 * kNvScaleStride);
+
+  // staging role: thread (sr, sq) converts bytes 16 sq .. 16 sq + 15 of token
+  // row sr of each step (fp16 chunks 2 sq, 2 sq + 1); rows past the expert's
+  // last pair repeat that pair's row (computed, dropped)
+  const int sr = threadIdx.x >> 3, sq = threadIdx.x & 7;
+  const int sslot = min(m0 + sr, n_e - 1);
+  const int64_t stok = (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + sslot] / p.top_k)
+                                   : (int64_t)(off_e + sslot);
+  const uint8_t* xsrc = p.a + stok * K + 16 * sq;
+  const int xc0 = sr * 256 + ((2 * sq) ^ (sr & 15)) * 16;
+  const int xc1 = sr * 256 + ((2 * sq + 1) ^ (sr & 15)) * 16;
+
+  // tile-long LDS tables: the 64 tokens' activation scales, this wave's
+  // weight scale lines (pieces past a line's end clamp to its last 16
+  // bytes: same data, same place)
+  {
+    const int b0 = min(4 * sq, S - 4);
+    *reinterpret_cast<uint32_t*>(&bsl[sr][b0]) =
+        *reinterpret_cast<const uint32_t*>(p.a_scale + stok * S + b0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pos = min(64 * grp + 16 * j, 8 * S - 16);
+        *reinterpret_cast<v4u*>(lds_sc + (16 * t + col) * kNvScaleStride + pos) =
+            *reinterpret_cast<const v4u*>(srow[t] + pos);
+      }
+  }
+
+  v4f acc[2][4];   // [weight tile][16-pair sub-tile]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4u A[4][2];     // weight ring: [step][tile]
+  v4u R;           // the 16 activation bytes of the next step to stage
+  auto load_w = [&](int s, v4u (&a)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
+  };
+  auto load_x = [&](int s) { R = *reinterpret_cast<const v4u*>(xsrc + (size_t)s * 128); };
+  auto store_x = [&](int buf) {
+    *reinterpret_cast<h8*>(&xl[buf][xc0]) = fp8x8_to_f16(R.x, R.y);
+    *reinterpret_cast<h8*>(&xl[buf][xc1]) = fp8x8_to_f16(R.z, R.w);
+  };
+  // one K step from the weight ring slot a and LDS buffer buf: MFMA j of a
+  // 16 x 16 tile takes elements 32 grp + 8 j .. +7 of the step
+  auto compute = [&](int s, const v4u (&a)[2], int buf) {
+    h8 wb[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t raw = *reinterpret_cast<const uint16_t*>(
+          lds_sc + (16 * t + col) * kNvScaleStride + 8 * s + 2 * grp);
+      const h2 ws = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false);
+      wb[t][0] = fp4x8_to_f16(a[t].x, ws[0]);
+      wb[t][1] = fp4x8_to_f16(a[t].y, ws[0]);
+      wb[t][2] = fp4x8_to_f16(a[t].z, ws[1]);
+      wb[t][3] = fp4x8_to_f16(a[t].w, ws[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * m + col;
+      const uint8_t* xr = &xl[buf][r * 256];
+      h8 bo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bo[j] = *reinterpret_cast<const h8*>(xr + ((4 * grp + j) ^ (r & 15)) * 16);
+      const float sx = __uint_as_float((uint32_t)bsl[r][s] << 23);   // 2^(code - 127)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        v4f part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb[t][j], bo[j], part, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][m][v] = __builtin_fmaf(part[v], sx, acc[t][m][v]);
+      }
+    }
+  };
+  // one group of four steps; LOAD: refill the weight ring with the next group
+  // (two steps at a time: both halves of each 128-byte line back to back)
+  auto group = [&](int s0, auto load) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int s = s0 + d;
+      compute(s, A[d], s & 1);
+      store_x((s + 1) & 1);                 // step s + 1 (the last step's copy is unused)
+      load_x(min(s + 2, S - 1));
+      if constexpr (decltype(load)::value) {
+        if (d & 1) {
+          load_w(s0 + 3 + d, A[d - 1]);
+          load_w(s0 + 4 + d, A[d]);
+        }
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);   // no work moved across steps
+    }
+  };
+
+  load_x(0);
+  store_x(0);
+  load_x(min(1, S - 1));
+#pragma unroll
+  for (int d = 0; d < 4; ++d) load_w(d, A[d]);
+  __syncthreads();
+  for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
+  group(S - 4, std::false_type{});
+
+  // lane holds acc[t][m][v] = output (weight row 4 grp + v of tile t, token
+  // 16 m + col)
+  if (MODE == 1) {
+    const float lim = p.limit;
+    float h[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float a = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = fminf(fmaxf(acc[0][m][v], -lim), lim);
+        const float u = fminf(fmaxf(acc[1][m][v], -lim), lim);
+        h[m][v] = silu_nv(g) * u;
+        a = fmaxf(a, fabsf(h[m][v]));
+      }
+      a = fmaxf(a, __shfl_xor(a, 16));
+      a = fmaxf(a, __shfl_xor(a, 32));
+      if (lane < 16) red[wv][16 * m + col] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tok = 16 * m + col;
+      if (m0 + tok >= n_e) continue;
+      float bmax = red[0][tok];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) bmax = fmaxf(bmax, red[w][tok]);
+      const int ex = pow2_scale_exp(bmax);
+      const size_t row = (size_t)(off_e + m0 + tok);
+      uint32_t word = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[m][v], -ex)) << (8 * v);
+      *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 16 * wv + 4 * grp) = word;
+      if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+    }
+  } else {
+    if (n0 + 32 * wv >= N) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tok = 16 * m + col;
+      if (m0 + tok >= n_e) continue;
+      const size_t row = (size_t)(off_e + m0 + tok);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const size_t c = (size_t)n0 + 32 * wv + 16 * t + 4 * grp;
+        if (p.out_fp32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
+              make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+        } else {
+          const uint32_t lo = f32_to_bf16(acc[t][m][0]) | (f32_to_bf16(acc[t][m][1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[t][m][2]) | (f32_to_bf16(acc[t][m][3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
+              make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
 static unsigned pad8_nv(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
 
 template <int MODE>
-static hipError_t launch_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
+static hipError_t launch_nv(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
   if (a.K % 512) return hipErrorInvalidValue;
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8_nv((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
-  if (a.K <= 4096)
+  if (bm == kNvM) {
+    if (a.K > 4096) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((expert_gemm_nv_m64<MODE>), dim3(grid), dim3(kNvMThreads), 0, st, a,
+                       mt_max, n_tiles);
+  } else if (bm != 16) {
+    return hipErrorInvalidValue;
+  } else if (a.K <= 4096)
     hipLaunchKernelGGL((expert_gemm_nv<MODE, true>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);
   else
@@ -337,11 +564,11 @@ static hipError_t launch_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st)
   return hipGetLastError();
 }
 
-hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
-  return launch_nv<1>(a, mt_max, st);
+hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
+  return launch_nv<1>(a, bm, mt_max, st);
 }
-hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st) {
-  return launch_nv<2>(a, mt_max, st);
+hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
+  return launch_nv<2>(a, bm, mt_max, st);
 }
 
 }  // namespace moe

@@ -172,9 +172,10 @@ struct ExpertGemmArgs {
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
 hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
-// NVFP4 weights (E4M3 scale per 16), m-tiles of 16 pairs, K % 512 == 0.
-hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
-hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int mt_max, hipStream_t st);
+// NVFP4 weights (E4M3 scale per 16), K % 512 == 0; m-tiles of bm = 16 pairs,
+// or 64 when K <= 4096.
+hipError_t launch_expert_gemm1_nv(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
+hipError_t launch_expert_gemm2_nv(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 // W4AFP8 weights (INT4 + float32 scale per 128), K % 512 == 0; m-tiles of
 // bm = 16 pairs, or 64 when K <= 4096.
 hipError_t launch_expert_gemm1_w4(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
