@@ -37,6 +37,9 @@ def _eager(L, x, ids, cfg):
     ("decode", None, {}),                                                   # full decode shape
     ("tiny", 40, dict(hidden=512, inter=256, n_experts=12, top_k=3, shared=True)),
     ("tiny", 33, dict(mode="hash", n_experts=20, top_k=6, hidden=384, inter=256, shared=True)),
+    # 600 tokens x top-8: the shared expert forks before routing, the router
+    # GEMM is split along K, the multi-kernel permutation, 128-pair tiles
+    ("decode", 600, dict(hidden=1024, inter=1024, n_experts=128, top_k=8)),
 ])
 def test_graph_replays_match_eager(name, tokens, over):
     wl, inp, d, L = _setup(name, tokens, **over)
