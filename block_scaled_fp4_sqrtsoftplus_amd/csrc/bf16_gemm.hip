@@ -401,31 +401,35 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
   const int nb = blockIdx.x;
   const size_t row_bytes = (size_t)K * 2;
 
-  // staging: thread tid moves chunks 4h..4h+3 of row r (r = tid % 128,
-  // h = tid / 128) of both operands, chunk c to slot c ^ (r & 7)
-  const int sr = tid & 127, sh = tid >> 7;
-  const uint8_t* wsrc;
-  if (EPI == EPI_SWIGLU) {
-    const int c = nb * 64 + (sr & 63);
-    wsrc = reinterpret_cast<const uint8_t*>(sr < 64 ? W : W3) + (size_t)c * row_bytes;
-  } else {
-    wsrc = reinterpret_cast<const uint8_t*>(W) + (size_t)(nb * 128 + sr) * row_bytes;
-  }
-  const int64_t xr = m0 + sr < M ? m0 + sr : M - 1;   // rows past M repeat row M-1 (dropped)
-  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(X) + (size_t)xr * row_bytes;
-  const size_t kofs = (size_t)blockIdx.z * kc * 2;    // this split's first K byte
-  wsrc += kofs;
-  xsrc += kofs;
+  // staging: load j of thread tid moves chunk c = tid % 8 of row
+  // r = tid / 8 + 32 j of both operands (eight threads cover a row's 128-byte
+  // step line, so one wave's load touches 8 lines), chunk c to LDS slot
+  // c ^ (r & 7)
+  const int sc = tid & 7;
+  const size_t kofs = (size_t)blockIdx.z * kc * 2 + 16 * sc;   // this split's first K byte
+  const uint8_t* wsrc[4];
+  const uint8_t* xsrc[4];
   uint32_t soff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) soff[j] = sr * kBfTileLine + 16 * ((4 * sh + j) ^ (sr & 7));
+  for (int j = 0; j < 4; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    if (EPI == EPI_SWIGLU) {
+      const int c = nb * 64 + (r & 63);
+      wsrc[j] = reinterpret_cast<const uint8_t*>(r < 64 ? W : W3) + (size_t)c * row_bytes + kofs;
+    } else {
+      wsrc[j] = reinterpret_cast<const uint8_t*>(W) + (size_t)(nb * 128 + r) * row_bytes + kofs;
+    }
+    const int64_t xr = m0 + r < M ? m0 + r : M - 1;   // rows past M repeat row M-1 (dropped)
+    xsrc[j] = reinterpret_cast<const uint8_t*>(X) + (size_t)xr * row_bytes + kofs;
+    soff[j] = r * kBfTileLine + 16 * (sc ^ (r & 7));
+  }
   // (native vector types: loops of struct copies would go through memory)
   v4i ga[4], gb[4];
   auto gload = [&](int s) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ga[j] = *reinterpret_cast<const v4i*>(wsrc + (size_t)s * kBfTileLine + 16 * (4 * sh + j));
-      gb[j] = *reinterpret_cast<const v4i*>(xsrc + (size_t)s * kBfTileLine + 16 * (4 * sh + j));
+      ga[j] = *reinterpret_cast<const v4i*>(wsrc[j] + (size_t)s * kBfTileLine);
+      gb[j] = *reinterpret_cast<const v4i*>(xsrc[j] + (size_t)s * kBfTileLine);
     }
   };
   auto lstore = [&](int buf) {
