@@ -47,6 +47,8 @@
 // together there, and share that XCD's L2.
 #include "moe_internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace moe {
@@ -55,6 +57,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // acc += (A * 2^(sa-127)) x (B * 2^(sb-127)) per 32-element K block; A is 32
 // FP4 values per lane (cbsz 4), B 32 FP8 values per lane (blgp 0), scale
@@ -94,8 +97,6 @@ __device__ __forceinline__ v4f mfma_fp8_fp8(const uint4& a0, const uint4& a1, co
       : "v"(av), "v"(bv), "v"(sa), "v"(sb));
   return acc;
 }
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // Maps the workgroup to (n_tile, expert, m0); returns false when idle.
 __device__ __forceinline__ bool map_tile(const ExpertGemmArgs& p, int mt_max, int n_tiles, int bm,
@@ -327,9 +328,9 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float g = fminf(fmaxf(acc[tt][m][v], -lim), lim);
-          const float u = fminf(fmaxf(acc[tt + 2][m][v], -lim), lim);
-          const float hv = silu_f(g) * u;
+          const float g = clamp_sym(acc[tt][m][v], lim);
+          const float u = clamp_sym(acc[tt + 2][m][v], lim);
+          const float hv = silu_fast(g) * u;
           h[m][tt][v] = hv;
           amax = fmaxf(amax, fabsf(hv));
         }
@@ -348,9 +349,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
         const size_t row = (size_t)(off_e + slot);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[m][tt][v], -ex)) << (8 * v);
+          const uint32_t word = e4m3x4_exp(h[m][tt], ex);
           *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
         }
         if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
@@ -535,9 +534,9 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
-        const float hv = silu_f(g) * u;
+        const float g = clamp_sym(acc[tt][v], lim);
+        const float u = clamp_sym(acc[tt + 2][v], lim);
+        const float hv = silu_fast(g) * u;
         h[tt][v] = hv;
         amax = fmaxf(amax, fabsf(hv));
       }
@@ -551,9 +550,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
       const size_t row = (size_t)(off_e + m0 + col);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[tt][v], -ex)) << (8 * v);
+        const uint32_t word = e4m3x4_exp(h[tt], ex);
         *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
       }
       if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
@@ -693,9 +690,9 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream8(ExpertGemmAr
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
-        const float hv = silu_f(g) * u;
+        const float g = clamp_sym(acc[tt][v], lim);
+        const float u = clamp_sym(acc[tt + 2][v], lim);
+        const float hv = silu_fast(g) * u;
         h[tt][v] = hv;
         amax = fmaxf(amax, fabsf(hv));
       }
@@ -709,9 +706,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream8(ExpertGemmAr
       const size_t row = (size_t)(off_e + m0 + col);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[tt][v], -ex)) << (8 * v);
+        const uint32_t word = e4m3x4_exp(h[tt], ex);
         *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
       }
       if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
@@ -869,6 +864,97 @@ __device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4]
         "n"(5 * TROW), "n"(6 * TROW), "n"(7 * TROW), "n"(WROW), "n"(2 * WROW), "n"(3 * WROW));
 }
 
+// The last 8 MFMAs of a step (sub-tiles 6, 7) with the next step's LDS work
+// in their shadow: after the first four, the reads of the next step's first
+// two sub-tiles (buffer offset OFFN) into n0, n1, and the LDS stores of this
+// thread's staged activation registers r (at wa + WOFF + 1024 * j); with SC
+// also the next group's scale lines, as tile_read_scales (into tw, ww).
+// Every scale register of the step is an input, so that none is reused
+// before the closing 32 wait states; then the LDS wait.
+#define TILE_LAST_MFMA4(C0, C1, C2, C3, B, T)                                                 \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C0 "], %[a0], %[" B "], %[" C0 "], %[s0], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C1 "], %[a1], %[" B "], %[" C1 "], %[s1], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C2 "], %[a2], %[" B "], %[" C2 "], %[s2], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C3 "], %[a3], %[" B "], %[" C3 "], %[s3], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t"
+#define TILE_LAST_LDS                                \
+  "ds_read_b128 %[x0], %[lo] offset:%[o0]\n\t"       \
+  "ds_read_b128 %[x1], %[hi] offset:%[o0]\n\t"       \
+  "ds_read_b128 %[y0], %[lo] offset:%[o1]\n\t"       \
+  "ds_read_b128 %[y1], %[hi] offset:%[o1]\n\t"       \
+  "ds_write_b128 %[wa], %[r0] offset:%[w0]\n\t"      \
+  "ds_write_b128 %[wa], %[r1] offset:%[w1]\n\t"      \
+  "ds_write_b128 %[wa], %[r2] offset:%[w2]\n\t"      \
+  "ds_write_b128 %[wa], %[r3] offset:%[w3]\n\t"
+#define TILE_LAST_SCALES                              \
+  "ds_read_b32 %[tw0], %[tok]\n\t"                    \
+  "ds_read_b32 %[tw1], %[tok] offset:%[q1]\n\t"       \
+  "ds_read_b32 %[tw2], %[tok] offset:%[q2]\n\t"       \
+  "ds_read_b32 %[tw3], %[tok] offset:%[q3]\n\t"       \
+  "ds_read_b32 %[tw4], %[tok] offset:%[q4]\n\t"       \
+  "ds_read_b32 %[tw5], %[tok] offset:%[q5]\n\t"       \
+  "ds_read_b32 %[tw6], %[tok] offset:%[q6]\n\t"       \
+  "ds_read_b32 %[tw7], %[tok] offset:%[q7]\n\t"       \
+  "ds_read_b128 %[ww0], %[wrow]\n\t"                  \
+  "ds_read_b128 %[ww1], %[wrow] offset:%[p1]\n\t"     \
+  "ds_read_b128 %[ww2], %[wrow] offset:%[p2]\n\t"     \
+  "ds_read_b128 %[ww3], %[wrow] offset:%[p3]\n\t"
+#define TILE_LAST_CLOSE "s_nop 15\n\ts_nop 15\n\ts_waitcnt lgkmcnt(0)"
+#define TILE_LAST_OUT                                                                          \
+  [c0] "+a"(c0[0]), [c1] "+a"(c0[1]), [c2] "+a"(c0[2]), [c3] "+a"(c0[3]), [d0] "+a"(c1[0]),    \
+      [d1] "+a"(c1[1]), [d2] "+a"(c1[2]), [d3] "+a"(c1[3]), [x0] "=&v"(x0), [x1] "=&v"(x1),    \
+      [y0] "=&v"(y0), [y1] "=&v"(y1)
+#define TILE_LAST_IN                                                                           \
+  [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0), [b1] "v"(b1),  \
+      [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]), [t6] "v"(sb[6]),     \
+      [t7] "v"(sb[7]), [k0] "v"(sb[0]), [k1] "v"(sb[1]), [k2] "v"(sb[2]), [k3] "v"(sb[3]),     \
+      [k4] "v"(sb[4]), [k5] "v"(sb[5]), [lo] "v"(lo), [hi] "v"(hi), [o0] "n"(OFFN),            \
+      [o1] "n"(OFFN + 2048), [wa] "v"(wa), [r0] "v"(r[0]), [r1] "v"(r[1]), [r2] "v"(r[2]),     \
+      [r3] "v"(r[3]), [w0] "n"(WOFF), [w1] "n"(WOFF + 1024), [w2] "n"(WOFF + 2048),             \
+      [w3] "n"(WOFF + 3072)
+template <int OFFN, int WOFF, bool SC, int TROW, int WROW>
+__device__ __forceinline__ void tile_mfma8_last_pf(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+                                                   const v8i& b0, const v8i& b1,
+                                                   const int (&sa)[4], const int (&sb)[8],
+                                                   v8i& n0, v8i& n1, uint32_t lo, uint32_t hi,
+                                                   const v4i (&r)[4], uint32_t wa,
+                                                   uint32_t (&tw)[8], v4i (&ww)[4], uint32_t tok,
+                                                   uint32_t wrow) {
+  v4i x0, x1, y0, y1;
+  if constexpr (SC) {
+    asm volatile("s_nop 1\n\t"
+                 TILE_LAST_MFMA4("c0", "c1", "c2", "c3", "b0", "t6")
+                 TILE_LAST_LDS
+                 TILE_LAST_SCALES
+                 TILE_LAST_MFMA4("d0", "d1", "d2", "d3", "b1", "t7")
+                 TILE_LAST_CLOSE
+                 : TILE_LAST_OUT, [tw0] "=&v"(tw[0]), [tw1] "=&v"(tw[1]), [tw2] "=&v"(tw[2]),
+                   [tw3] "=&v"(tw[3]), [tw4] "=&v"(tw[4]), [tw5] "=&v"(tw[5]), [tw6] "=&v"(tw[6]),
+                   [tw7] "=&v"(tw[7]), [ww0] "=&v"(ww[0]), [ww1] "=&v"(ww[1]), [ww2] "=&v"(ww[2]),
+                   [ww3] "=&v"(ww[3])
+                 : TILE_LAST_IN, [tok] "v"(tok), [wrow] "v"(wrow), [q1] "n"(TROW),
+                   [q2] "n"(2 * TROW), [q3] "n"(3 * TROW), [q4] "n"(4 * TROW), [q5] "n"(5 * TROW),
+                   [q6] "n"(6 * TROW), [q7] "n"(7 * TROW), [p1] "n"(WROW), [p2] "n"(2 * WROW),
+                   [p3] "n"(3 * WROW));
+  } else {
+    asm volatile("s_nop 1\n\t"
+                 TILE_LAST_MFMA4("c0", "c1", "c2", "c3", "b0", "t6")
+                 TILE_LAST_LDS
+                 TILE_LAST_MFMA4("d0", "d1", "d2", "d3", "b1", "t7")
+                 TILE_LAST_CLOSE
+                 : TILE_LAST_OUT
+                 : TILE_LAST_IN);
+    (void)tw; (void)ww; (void)tok; (void)wrow;
+  }
+  n0 = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  n1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+}
+#undef TILE_LAST_MFMA4
+#undef TILE_LAST_LDS
+#undef TILE_LAST_SCALES
+#undef TILE_LAST_CLOSE
+#undef TILE_LAST_OUT
+#undef TILE_LAST_IN
+
 // Workgroup barrier once this wave's LDS writes are done; no memory access
 // is moved across it (outstanding global loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
@@ -879,117 +965,192 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// Load of a T from global memory (the address space spelt out, so that the
+// compiler emits a global load even where it cannot trace the pointer).
+template <class T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// One tile of the persistent tile kernel: expert e, first weight row n0,
+// first pair slot m0 among the expert's n_e sorted pairs starting at off_e.
+struct TileSel {
+  int e, n0, m0, off_e, n_e;
+};
+
+// Tile u of the expert-major order (m-tile fastest; see map_tile_grouped)
+// from LDS copies of the m-tile prefix (mt) and the expert offsets (eo):
+// e is the number of entries mt[i] * n_tiles <= u, minus one, counted by the
+// whole wave at once.  Wave-uniform.
+__device__ __forceinline__ TileSel decode_tile(const int* mt, const int* eo, int E, int n_tiles,
+                                               int rows_per_tile, int u, int lane) {
+  int cnt = 0;
+#pragma unroll
+  for (int i0 = 0; i0 <= kMaxExperts; i0 += 64) {
+    const int i = i0 + lane;
+    const int v = mt[min(i, E)];  // unconditional: the reads overlap
+    cnt += __popcll(__ballot((i <= E) & (v * n_tiles <= u)));
+  }
+  TileSel t;
+  t.e = __builtin_amdgcn_readfirstlane(cnt - 1);
+  const int mt0 = __builtin_amdgcn_readfirstlane(mt[t.e]);
+  const int m_e = __builtin_amdgcn_readfirstlane(mt[t.e + 1]) - mt0;
+  const int local = u - mt0 * n_tiles;
+  const int n_tile = local / m_e;
+  t.n0 = n_tile * rows_per_tile;
+  t.m0 = (local - n_tile * m_e) * 128;
+  t.off_e = __builtin_amdgcn_readfirstlane(eo[t.e]);
+  t.n_e = __builtin_amdgcn_readfirstlane(eo[t.e + 1]) - t.off_e;
+  return t;
+}
+
+// Persistent tile kernel: one workgroup per CU walks its share of the tiles
+// (XCD x = blockIdx % 8 takes the x-th eighth of the expert-major tile list,
+// its workgroups every R-th tile of it) as one continuous stream of K steps:
+// the weight ring, the activation staging and the scale lines of the next
+// tile are loaded while the current tile finishes, so that its epilogue and
+// the next tile's first loads overlap instead of following each other.
 template <int MODE, int S>
-__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmArgs p, int mt_max,
+__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmArgs p,
                                                                      int n_tiles) {
   constexpr int MT = 8, BM = 128;
   constexpr int K = S * 128;
-  constexpr int SD = S / 4;
   static_assert(S % 4 == 0 && S >= 8, "K steps in groups of four, at least two groups");
-  __shared__ __attribute__((aligned(1024))) uint8_t act[4 * kTileBuf];
   constexpr int WLINE = 4 * S + 16;     // weight scale line, padded (banks)
-  __shared__ __attribute__((aligned(16))) uint8_t bsc[BM][S];
-  __shared__ __attribute__((aligned(16))) uint8_t wsc[4][64][WLINE];
+  constexpr int NROWS = MODE == 1 ? kG1Cols : kG2Rows;
+  __shared__ __attribute__((aligned(1024))) uint8_t act[4 * kTileBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t bsc[2][BM][S];
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[2][4][64][WLINE];
   __shared__ float red[4][BM];
-  (void)mt_max;
-
-  int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_grouped(p, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
+  __shared__ int tab_mt[kMaxExperts + 1];
+  __shared__ int tab_eo[kMaxExperts + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int N = p.N;
-  const size_t wrow_bytes = (size_t)K / 2;
-  const size_t srow_bytes = (size_t)K / 32;
+  const int N = p.N, E = p.E;
 
-  // weight rows of this wave (waves past N in GEMM2 read row 0 and skip the
-  // MFMAs: unconditional loads keep every wave's load count the same)
-  const uint8_t* wptr[4];
-  const uint8_t* sptr[4];
-  int n0;
-  bool wave_live = true;
-  if (MODE == 1) {
-    n0 = n_tile * kG1Cols;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
-      const uint8_t* base = (t < 2) ? p.w : p.w3;
-      const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
-      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes;
-    }
-  } else {
-    n0 = n_tile * kG2Rows;
-    wave_live = (n0 + 64 * wv) < N;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
-      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
-    }
+  for (int i = tid; i <= E; i += kGemmThreads) {
+    tab_mt[i] = p.mtile_off[i];
+    tab_eo[i] = p.expert_offsets[i];
   }
+  __syncthreads();
 
-  // activation source row of tile token t (slots past the expert's last pair
+  // tiles of this workgroup: u = lo + r + j * R, j = 0 .. n_my - 1
+  const int total = __builtin_amdgcn_readfirstlane(tab_mt[E]) * n_tiles;
+  const int share = (total + 7) >> 3;
+  const int R = gridDim.x >> 3;
+  const int r = blockIdx.x >> 3;
+  const int lo = (blockIdx.x & 7) * share;
+  const int hi = min(lo + share, total);
+  const int n_my = hi - lo > r ? (hi - lo - r + R - 1) / R : 0;
+  if (n_my <= 0) return;
+  auto tile_u = [&](int j) { return lo + r + j * R; };
+  auto decode = [&](int u) { return decode_tile(tab_mt, tab_eo, E, n_tiles, NROWS, u, lane); };
+
+  // Weight rows of this wave in a tile, as wave-uniform bases (row 16*t +
+  // col of the wave's 64 at lane offset col * K/2 + 16 * grp).  Waves past N
+  // in GEMM2 read rows 0..63 of the expert and skip the MFMAs: unconditional
+  // loads keep every wave's load count the same.
+  auto tile_bases = [&](const TileSel& ts, const uint8_t* (&wb)[4], const uint8_t* (&sb)[4]) {
+    bool live = true;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      int row0;
+      const uint8_t* wbase = p.w;
+      const uint8_t* sbase = p.w_scale;
+      if (MODE == 1) {
+        row0 = ts.n0 + 32 * wv + 16 * (t & 1);
+        if (t >= 2) {
+          wbase = p.w3;
+          sbase = p.w3_scale;
+        }
+      } else {
+        live = ts.n0 + 64 * wv < N;
+        row0 = live ? ts.n0 + 64 * wv + 16 * t : 16 * t;
+      }
+      const size_t rr = (size_t)ts.e * N + row0;
+      wb[t] = wbase + rr * (K / 2);
+      sb[t] = sbase + rr * (K / 32);
+    }
+    return live;
+  };
+  const uint32_t wlo = (uint32_t)(col * (K / 2) + 16 * grp);
+  const uint32_t slo = (uint32_t)(col * (K / 32) + S * grp);
+
+  // activation staging: this thread moves 4 x 16 bytes per step, for tile
+  // tokens 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the
+  // token's line, i.e. chunk tile_slot(token, lane%8) of the step (the map
+  // is an involution on the chunk index)
+  const int a_slot = tile_slot(lane >> 3, lane & 7);
+  auto stage_tok = [&](int j) { return 32 * wv + 8 * j + (lane >> 3); };
+  // sorted-pair slot of tile token t (slots past the expert's last pair
   // read that last pair's row; their results are dropped)
-  auto src_row = [&](int t) -> int64_t {
-    const int slot = min(m0 + t, n_e - 1);
-    return (MODE == 1) ? (int64_t)(p.sorted_pairs[off_e + slot] / p.top_k)
-                       : (int64_t)(off_e + slot);
-  };
-
-  // Activation staging: this thread moves 4 x 16 bytes per step, for tokens
-  // 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the token's
-  // line, i.e. chunk tile_slot(t, lane%8) of the step (the map is an
-  // involution on the chunk index)
-  const uint8_t* ssrc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 32 * wv + 8 * j + (lane >> 3);
-    ssrc[j] = p.a + src_row(t) * K + 16 * tile_slot(t, lane & 7);
-  }
+  auto pair_slot = [&](const TileSel& ts, int t) { return ts.off_e + min(ts.m0 + t, ts.n_e - 1); };
   const int sdst = (32 * wv + (lane >> 3)) * 128 + 16 * (lane & 7);  // + 1024 * j
-  v4i R[2][4];
-  auto stage_load = [&](int s, v4i (&r)[4]) {
+  auto stage_load = [&](const uint8_t* const (&src)[4], int s, v4i (&rg)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const v4i*>(ssrc[j] + (size_t)s * 128);
+    for (int j = 0; j < 4; ++j) rg[j] = gload<v4i>(src[j] + (size_t)s * 128);
   };
-  auto stage_store = [&](int q, const v4i (&r)[4]) {
+  auto stage_store = [&](int q, const v4i (&rg)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<v4i*>(act + q * kTileBuf + sdst + 1024 * j) = r[j];
+      *reinterpret_cast<v4i*>(act + q * kTileBuf + sdst + 1024 * j) = rg[j];
+  };
+  v4i A[4][4];  // weight ring: [step % 4][tile]
+  auto load_a = [&](const uint8_t* const (&wb)[4], int s, v4i (&a)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = gload<v4i>(wb[t] + wlo + s * 64);
   };
 
-  // token scales of the whole tile into LDS: thread tid copies half of
-  // token tid/2's scale line
-  {
-    const int st_tok = tid >> 1, st_half = tid & 1;
-    const uint8_t* src = p.a_scale + src_row(st_tok) * S + st_half * (S / 2);
-    uint8_t* dst = &bsc[st_tok][st_half * (S / 2)];
-    if constexpr (S == 32) {
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-    } else if constexpr (S == 16) {
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-    }
-  }
+  // Scale lines: thread (wv, lane) copies bytes S*grp .. S*grp + S - 1 of the
+  // line of row 16*t + col of its wave (t = 0..3) and half of the token scale
+  // line of tile token tid/2.
+  typedef typename std::conditional<S == 8, v2i, v4i>::type SChunk;
+  constexpr int SN = S == 8 ? 1 : S / 16;
+  struct WLine { SChunk c[SN]; };
+  auto wline_load = [&](const uint8_t* src) {
+    WLine w;
+#pragma unroll
+    for (int k = 0; k < SN; ++k) w.c[k] = gload<SChunk>(src + slo + k * sizeof(SChunk));
+    return w;
+  };
+  auto wline_store = [&](int b, int t, const WLine& w) {
+#pragma unroll
+    for (int k = 0; k < SN; ++k)
+      reinterpret_cast<SChunk*>(&wsc[b][wv][16 * t + col][S * grp])[k] = w.c[k];
+  };
+  typedef typename std::conditional<S == 32, v4i, typename std::conditional<S == 16, v2i, int>::type>::type TChunk;
+  auto tline_src = [&](int row) { return p.a_scale + (size_t)row * S + (tid & 1) * (S / 2); };
+  auto tline_store = [&](int b, const TChunk& v) {
+    *reinterpret_cast<TChunk*>(&bsc[b][tid >> 1][(tid & 1) * (S / 2)]) = v;
+  };
 
-  // weight scale lines into LDS (a quarter per lane group): row 16*t + col
-  // of this wave's 64
+  // ---- first tile: scale lines and the start of the pipeline ----
+  TileSel cur = decode(tile_u(0));
+  const uint8_t* wb[4];
+  const uint8_t* sb[4];
+  bool live = tile_bases(cur, wb, sb);
+  const uint8_t* ssrc[4];
+  {
+    int rows[4];
+    int srow;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint8_t* src = sptr[t] + grp * S;
-    uint8_t* dst = &wsc[wv][16 * t + col][grp * S];
-    if constexpr (S >= 16) {
-#pragma unroll
-      for (int j = 0; j < S / 16; ++j)
-        reinterpret_cast<uint4*>(dst)[j] = reinterpret_cast<const uint4*>(src)[j];
-    } else {
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    for (int j = 0; j < 4; ++j) {
+      const int ps = pair_slot(cur, stage_tok(j));
+      rows[j] = MODE == 1 ? p.sorted_pairs[ps] / p.top_k : ps;
     }
+    {
+      const int ps = pair_slot(cur, tid >> 1);
+      srow = MODE == 1 ? p.sorted_pairs[ps] / p.top_k : ps;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ssrc[j] = p.a + (size_t)rows[j] * K + 16 * a_slot;
+    tline_store(0, gload<TChunk>(tline_src(srow)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wline_store(0, t, wline_load(sb[t]));
   }
 
   v4f acc[MT][4];
@@ -998,158 +1159,284 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[m][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v4i A[4][4];  // weight ring: [step % 4][tile]
-  auto load_a = [&](int s, v4i (&a)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4i*>(wptr[t] + (size_t)s * 64);
-  };
+  // Activations run three steps ahead: buffers 0 and 1 are written here and
+  // step 2 waits in registers; the first group's scales and the first two
+  // sub-tiles of step 0 are read before the loop, later ones by the step
+  // before (in the shadow of its last MFMAs).
+  v4i R2[2][4];
+  load_a(wb, 0, A[0]);
+  stage_load(ssrc, 0, R2[0]);
+  load_a(wb, 1, A[1]);
+  stage_load(ssrc, 1, R2[1]);
+  load_a(wb, 2, A[2]);
+  load_a(wb, 3, A[3]);
+  stage_store(0, R2[0]);
+  stage_store(1, R2[1]);
+  stage_load(ssrc, 2, R2[0]);
 
-  // per-lane LDS addresses
   const int rslot = tile_slot(col, grp);
   const uint32_t rd_lo = lds_addr(act) + col * 128 + 16 * rslot;
   const uint32_t rd_hi = rd_lo ^ 64u;
-  const uint32_t sc_tok = lds_addr(&bsc[col][0]);
-  const uint32_t sc_w = lds_addr(&wsc[wv][col][0]);
-
+  const uint32_t st_wa = lds_addr(act) + sdst;
   uint32_t sbw[MT];
   v4i saw[4];
-  // one K step from buffer Q (compile-time) and ring slot Q
-  auto compute = [&](int s, auto qc) {
-    constexpr int Q = decltype(qc)::value;
-    if (!wave_live) return;
-    if (Q == 0) tile_read_scales<16 * S, 16 * WLINE>(sbw, saw, sc_tok + s, sc_w + 4 * s);
-    const int sa[4] = {saw[0][Q] >> (8 * grp), saw[1][Q] >> (8 * grp), saw[2][Q] >> (8 * grp),
-                       saw[3][Q] >> (8 * grp)};
-    const int sh = 8 * Q;
-    const int sb[8] = {(int)(sbw[0] >> sh), (int)(sbw[1] >> sh), (int)(sbw[2] >> sh),
-                       (int)(sbw[3] >> sh), (int)(sbw[4] >> sh), (int)(sbw[5] >> sh),
-                       (int)(sbw[6] >> sh), (int)(sbw[7] >> sh)};
-    constexpr int B = Q * kTileBuf;
-    v8i x0, x1, y0, y1;
-    // one guard per step: every scale register of the step stays live until
-    // the last block, which closes with the wait states
-    tile_read2<B>(x0, x1, rd_lo, rd_hi);
-    tile_mfma8_read<B + 2 * 2048>(acc[0], acc[1], A[Q], x0, x1, sa, sb[0], sb[1], y0,
-                                               y1, rd_lo, rd_hi);
-    tile_mfma8_read<B + 4 * 2048>(acc[2], acc[3], A[Q], y0, y1, sa, sb[2], sb[3], x0,
-                                               x1, rd_lo, rd_hi);
-    tile_mfma8_read<B + 6 * 2048>(acc[4], acc[5], A[Q], x0, x1, sa, sb[4], sb[5], y0,
-                                               y1, rd_lo, rd_hi);
-    tile_mfma8_last(acc[6], acc[7], A[Q], y0, y1, sa, sb, x0, x1);
-  };
+  v8i x0, x1;
+  lds_barrier();
+  tile_read_scales<16 * S, 16 * WLINE>(sbw, saw, lds_addr(&bsc[0][col][0]),
+                                       lds_addr(&wsc[0][wv][col][0]));
+  tile_read2<0>(x0, x1, rd_lo, rd_hi);
 
-  // Pipeline, step s: barrier; activation loads for step s+2; compute(s)
-  // from buffer s%4 and ring slot s%4; weight loads for step s+4 into that
-  // slot; step s+1's activations (loaded during step s-1) written to buffer
-  // (s+1)%4, last read in step s-3.  Nothing past the last step is loaded.
-  load_a(0, A[0]);
-  stage_load(0, R[0]);
-  load_a(1, A[1]);
-  stage_load(1, R[1]);
-  load_a(2, A[2]);
-  load_a(3, A[3]);
-  stage_store(0, R[0]);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-#define TILE_STEP(s, QC)                                          \
-  do {                                                            \
-    constexpr int q_ = QC::value;                                 \
-    lds_barrier();                                                \
-    if ((s) + 2 < S) stage_load((s) + 2, R[q_ & 1]);              \
-    compute((s), QC{});                                           \
-    if ((s) + 4 < S) load_a((s) + 4, A[q_]);                      \
-    if ((s) + 1 < S) stage_store((q_ + 1) & 3, R[(q_ + 1) & 1]);  \
-  } while (0)
-  for (int s0 = 0; s0 < S - 4; s0 += 4) {
-    TILE_STEP(s0, I0);
-    TILE_STEP(s0 + 1, I1);
-    TILE_STEP(s0 + 2, I2);
-    TILE_STEP(s0 + 3, I3);
-  }
-  TILE_STEP(S - 4, I0);
-  TILE_STEP(S - 3, I1);
-  TILE_STEP(S - 2, I2);
-  TILE_STEP(S - 1, I3);
-#undef TILE_STEP
-  // the epilogue reads the accumulators only after the last block's wait
-  // states (the MFMAs are invisible to the compiler's hazard tracking)
-  asm volatile(""
-               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
-                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
-                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
-                 "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
-  asm volatile(""
-               : "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]), "+a"(acc[4][3]),
-                 "+a"(acc[5][0]), "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]),
-                 "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3]),
-                 "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]));
 
-  if (MODE == 1) {
-    // clamped SwiGLU, per-128 FP8 requant of h over this tile's 128 columns
-    const float lim = p.limit;
+  for (int jt = 0; jt < n_my; ++jt) {
+    const int cb = jt & 1, nb = cb ^ 1;  // scale buffers of this and the next tile
+    const uint32_t sc_tok = lds_addr(&bsc[cb][col][0]);
+    const uint32_t sc_w = lds_addr(&wsc[cb][wv][col][0]);
+
+    const uint32_t nsc_tok = lds_addr(&bsc[nb][col][0]);
+    const uint32_t nsc_w = lds_addr(&wsc[nb][wv][col][0]);
+
+    // One K step from buffer Q (compile-time) and ring slot Q; its operands
+    // for sub-tiles 0, 1 (x0, x1) and, at Q == 0, the group's scales were
+    // read by the step before.  The last block also writes the activations
+    // of step s + 2 to their buffer and, at Q == 3, reads the next group's
+    // scales (the next tile's first group after its last step).
+    auto compute = [&](int s, auto qc, auto lastc) {
+      constexpr int Q = decltype(qc)::value;
+      constexpr bool LAST = decltype(lastc)::value;  // s == S - 1
+      constexpr int WB = ((Q + 2) & 3) * kTileBuf;
+      if (!live) {
+        stage_store((Q + 2) & 3, R2[Q & 1]);
+        return;
+      }
+      const int sa[4] = {saw[0][Q] >> (8 * grp), saw[1][Q] >> (8 * grp), saw[2][Q] >> (8 * grp),
+                         saw[3][Q] >> (8 * grp)};
+      const int sh = 8 * Q;
+      const int sbv[8] = {(int)(sbw[0] >> sh), (int)(sbw[1] >> sh), (int)(sbw[2] >> sh),
+                          (int)(sbw[3] >> sh), (int)(sbw[4] >> sh), (int)(sbw[5] >> sh),
+                          (int)(sbw[6] >> sh), (int)(sbw[7] >> sh)};
+      constexpr int B = Q * kTileBuf;
+      constexpr int BN = ((Q + 1) & 3) * kTileBuf;
+      v8i y0, y1;
+      // one guard per step: every scale register of the step stays live
+      // until the last block, which closes with the wait states
+      tile_mfma8_read<B + 2 * 2048>(acc[0], acc[1], A[Q], x0, x1, sa, sbv[0], sbv[1], y0, y1,
+                                    rd_lo, rd_hi);
+      tile_mfma8_read<B + 4 * 2048>(acc[2], acc[3], A[Q], y0, y1, sa, sbv[2], sbv[3], x0, x1,
+                                    rd_lo, rd_hi);
+      tile_mfma8_read<B + 6 * 2048>(acc[4], acc[5], A[Q], x0, x1, sa, sbv[4], sbv[5], y0, y1,
+                                    rd_lo, rd_hi);
+      const uint32_t tok = LAST ? nsc_tok : sc_tok + s + 1;
+      const uint32_t wrow = LAST ? nsc_w : sc_w + 4 * (s + 1);
+      tile_mfma8_last_pf<BN, WB, Q == 3, 16 * S, 16 * WLINE>(acc[6], acc[7], A[Q], y0, y1, sa,
+                                                             sbv, x0, x1, rd_lo, rd_hi,
+                                                             R2[Q & 1], st_wa, sbw, saw, tok,
+                                                             wrow);
+    };
+
+    // The next tile (this one again after the last: its loads then only
+    // re-read valid rows), prepared in the first steps: P0 decode and pair
+    // rows, P1-P4 weight scale lines (stored one step after their load),
+    // P4 token scale line (stored at P5) and activation row pointers.
+    TileSel nxt;
+    const uint8_t* nwb[4];
+    const uint8_t* nsb[4];
+    bool nlive;
+    const uint8_t* nss[4];
+    int nraw[4], nraw_s;
+    WLine wtmp[2];  // loaded at P into [(P-1)&1], stored at P+1
+    TChunk ttmp;
+    auto prep_load = [&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      if constexpr (P == 0) {
+        nxt = decode(tile_u(jt + 1 < n_my ? jt + 1 : jt));
+        nlive = tile_bases(nxt, nwb, nsb);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float amax = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float g = fminf(fmaxf(acc[m][tt][v], -lim), lim);
-          const float u = fminf(fmaxf(acc[m][tt + 2][v], -lim), lim);
-          const float hv = silu_f(g) * u;
-          acc[m][tt][v] = hv;                       // h kept in the w1 slots
-          amax = fmaxf(amax, fabsf(hv));
+        for (int j = 0; j < 4; ++j) {
+          const int ps = pair_slot(nxt, stage_tok(j));
+          nraw[j] = MODE == 1 ? gload<int>(p.sorted_pairs + ps) : ps;
         }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      if (lane < 16) red[wv][16 * m + lane] = amax;
-    }
-    __syncthreads();
+        const int ps = pair_slot(nxt, tid >> 1);
+        nraw_s = MODE == 1 ? gload<int>(p.sorted_pairs + ps) : ps;
+      } else if constexpr (P >= 1 && P <= 4) {
+        wtmp[(P - 1) & 1] = wline_load(nsb[P - 1]);
+        if constexpr (P == 4) {
+          ttmp = gload<TChunk>(tline_src(MODE == 1 ? nraw_s / p.top_k : nraw_s));
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int tokc = 16 * m + col;
-      const float amax = fmaxf(fmaxf(red[0][tokc], red[1][tokc]), fmaxf(red[2][tokc], red[3][tokc]));
-      const int ex = pow2_scale_exp(amax);
-      const int slot = m0 + tokc;
-      if (slot < n_e) {
+          for (int j = 0; j < 4; ++j)
+            nss[j] = p.a + (size_t)(MODE == 1 ? nraw[j] / p.top_k : nraw[j]) * K + 16 * a_slot;
+        }
+      }
+    };
+    auto prep_store = [&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      if constexpr (P >= 2 && P <= 5) wline_store(nb, P - 2, wtmp[P & 1]);
+      if constexpr (P == 5) tline_store(nb, ttmp);
+    };
+
+    // Step s: barrier; activation loads for step s+3 into registers;
+    // compute(s) from buffer s%4 and ring slot s%4, writing step s+2's
+    // activations (loaded during step s-1) to buffer (s+2)%4 (last read in
+    // step s-2, before the barrier of step s-1); weight loads for step s+4
+    // into the ring slot.  Steps past the tile's last come from the next
+    // tile.  PREP: compile-time index of the next tile's preparation work;
+    // MID: a step of the middle loop (s + 4 < S).
+#define TILE_STEP(s, QC, PREP, MID)                                              \
+  do {                                                                           \
+    constexpr int q_ = QC::value;                                                \
+    lds_barrier();                                                               \
+    if ((MID) || (s) + 3 < S) stage_load(ssrc, (s) + 3, R2[(q_ + 1) & 1]);       \
+    else stage_load(nss, (s) + 3 - S, R2[(q_ + 1) & 1]);                         \
+    prep_load(std::integral_constant<int, PREP>{});                              \
+    compute((s), QC{}, std::integral_constant<bool, !(MID) && (s) == S - 1>{});  \
+    if ((MID) || (s) + 4 < S) load_a(wb, (s) + 4, A[q_]);                        \
+    else load_a(nwb, (s) + 4 - S, A[q_]);                                        \
+    prep_store(std::integral_constant<int, PREP>{});                             \
+  } while (0)
+    TILE_STEP(0, I0, 0, 0);
+    TILE_STEP(1, I1, 1, 0);
+    TILE_STEP(2, I2, 2, 0);
+    TILE_STEP(3, I3, 3, 0);
+    TILE_STEP(4, I0, 4, 0);
+    TILE_STEP(5, I1, 5, 0);
+    TILE_STEP(6, I2, 6, 0);
+    TILE_STEP(7, I3, 7, 0);
+    for (int s0 = 8; s0 < S - 4; s0 += 4) {
+      TILE_STEP(s0, I0, -1, 1);
+      TILE_STEP(s0 + 1, I1, -1, 1);
+      TILE_STEP(s0 + 2, I2, -1, 1);
+      TILE_STEP(s0 + 3, I3, -1, 1);
+    }
+    if constexpr (S > 8) {
+      TILE_STEP(S - 4, I0, -1, 0);
+      TILE_STEP(S - 3, I1, -1, 0);
+      TILE_STEP(S - 2, I2, -1, 0);
+      TILE_STEP(S - 1, I3, -1, 0);
+    }
+#undef TILE_STEP
+    // the epilogue reads the accumulators only after the last block's wait
+    // states (the MFMAs are invisible to the compiler's hazard tracking)
+    asm volatile(""
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+    asm volatile(""
+                 : "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]), "+a"(acc[4][3]),
+                   "+a"(acc[5][0]), "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]),
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3]),
+                   "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]));
+
+    const int m0 = cur.m0, off_e = cur.off_e, n_e = cur.n_e, n0 = cur.n0;
+    if (MODE == 1) {
+      // clamped SwiGLU, per-128 FP8 requant of h over this tile's 128 columns
+      const float lim = p.limit;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float amax = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float g = clamp_sym(acc[m][tt][v], lim);
+            const float u = clamp_sym(acc[m][tt + 2][v], lim);
+            const float hv = silu_fast(g) * u;
+            acc[m][tt][v] = hv;                       // h kept in the w1 slots
+            amax = fmaxf(amax, fabsf(hv));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        if (lane < 16) red[wv][16 * m + lane] = amax;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int tokc = 16 * m + col;
+        const float amax =
+            fmaxf(fmaxf(red[0][tokc], red[1][tokc]), fmaxf(red[2][tokc], red[3][tokc]));
+        const int ex = pow2_scale_exp(amax);
+        const int slot = m0 + tokc;
+        if (slot < n_e) {
+          const size_t row = (size_t)(off_e + slot);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const uint32_t word = e4m3x4_exp(acc[m][tt], ex);
+            *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
+          }
+          if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
+        }
+      }
+    } else if (live) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int slot = m0 + 16 * m + col;
+        if (slot >= n_e) continue;
         const size_t row = (size_t)(off_e + slot);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(acc[m][tt][v], -ex)) << (8 * v);
-          *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
-        }
-        if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
-      }
-    }
-  } else {
-    if (!wave_live) return;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int slot = m0 + 16 * m + col;
-      if (slot >= n_e) continue;
-      const size_t row = (size_t)(off_e + slot);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
-        if (p.out_fp32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
-              make_float4(acc[m][t][0], acc[m][t][1], acc[m][t][2], acc[m][t][3]);
-        } else {
-          const uint32_t lo = f32_to_bf16(acc[m][t][0]) | (f32_to_bf16(acc[m][t][1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[m][t][2]) | (f32_to_bf16(acc[m][t][3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
-              make_uint2(lo, hi);
+        for (int t = 0; t < 4; ++t) {
+          const size_t c = (size_t)n0 + 64 * wv + 16 * t + 4 * grp;
+          if (p.out_fp32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * N + c) =
+                make_float4(acc[m][t][0], acc[m][t][1], acc[m][t][2], acc[m][t][3]);
+          } else {
+            const uint32_t lo2 = f32_to_bf16(acc[m][t][0]) | (f32_to_bf16(acc[m][t][1]) << 16);
+            const uint32_t hi2 = f32_to_bf16(acc[m][t][2]) | (f32_to_bf16(acc[m][t][3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * N + c) =
+                make_uint2(lo2, hi2);
+          }
         }
       }
     }
+
+    // next tile
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the zeroed accumulators settle before the next tile's first MFMA
+    asm volatile("s_nop 1"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+    asm volatile("s_nop 1"
+                 : "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]), "+a"(acc[4][3]),
+                   "+a"(acc[5][0]), "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]),
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3]),
+                   "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]));
+    cur = nxt;
+    live = nlive;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wb[t] = nwb[t];
+      sb[t] = nsb[t];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ssrc[j] = nss[j];
   }
 }
 
 static inline unsigned pad8(int64_t g) { return (unsigned)((g + 7) / 8 * 8); }
+
+// Workgroups of a persistent launch: the device's CU count, rounded down to a
+// multiple of 8 (the XCD count), at least 8.
+static int persistent_workgroups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 8;
+    n = std::max(8, cus / 8 * 8);
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 template <int MODE>
 static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st) {
@@ -1178,15 +1465,18 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   }
   if (bm == 128) {
     if (a.K != 1024 && a.K != 2048 && a.K != 4096) return hipErrorInvalidValue;
+    if (a.E > kMaxExperts) return hipErrorInvalidValue;
+    // persistent: at most one workgroup per CU (the LDS use allows no more)
+    const unsigned pgrid = std::min(grid, (unsigned)persistent_workgroups());
     if (a.K == 4096)
-      hipLaunchKernelGGL((expert_gemm_tile<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
-                         mt_max, n_tiles);
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 32>), dim3(pgrid), dim3(kGemmThreads), 0, st, a,
+                         n_tiles);
     else if (a.K == 2048)
-      hipLaunchKernelGGL((expert_gemm_tile<MODE, 16>), dim3(grid), dim3(kGemmThreads), 0, st, a,
-                         mt_max, n_tiles);
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 16>), dim3(pgrid), dim3(kGemmThreads), 0, st, a,
+                         n_tiles);
     else
-      hipLaunchKernelGGL((expert_gemm_tile<MODE, 8>), dim3(grid), dim3(kGemmThreads), 0, st, a,
-                         mt_max, n_tiles);
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 8>), dim3(pgrid), dim3(kGemmThreads), 0, st, a,
+                         n_tiles);
   } else if (bm == 16 && a.K == 4096) {
     hipLaunchKernelGGL((expert_gemm_stream<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,
                        mt_max, n_tiles);

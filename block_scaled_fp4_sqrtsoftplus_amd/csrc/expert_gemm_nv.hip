@@ -34,8 +34,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float silu_nv(float g) { return g / (1.0f + expf(-g)); }
-
 // 8 E2M1 nibbles (low nibble first) times an fp16 scale -> 8 fp16
 __device__ __forceinline__ h8 fp4x8_to_f16(uint32_t w, _Float16 s) {
   const h2 sc = {s, s};
@@ -278,9 +276,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
-        const float hv = silu_nv(g) * u;
+        const float g = clamp_sym(acc[tt][v], lim);
+        const float u = clamp_sym(acc[tt + 2][v], lim);
+        const float hv = silu_fast(g) * u;
         h[tt][v] = hv;
         amax = fmaxf(amax, fabsf(hv));
       }
@@ -294,9 +292,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
       const size_t row = (size_t)(off_e + m0 + col);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[tt][v], -ex)) << (8 * v);
+        const uint32_t word = e4m3x4_exp(h[tt], ex);
         *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 32 * wv + 16 * tt + 4 * grp) = word;
       }
       if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
@@ -492,9 +488,9 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
       float a = 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float g = fminf(fmaxf(acc[0][m][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[1][m][v], -lim), lim);
-        h[m][v] = silu_nv(g) * u;
+        const float g = clamp_sym(acc[0][m][v], lim);
+        const float u = clamp_sym(acc[1][m][v], lim);
+        h[m][v] = silu_fast(g) * u;
         a = fmaxf(a, fabsf(h[m][v]));
       }
       a = fmaxf(a, __shfl_xor(a, 16));
@@ -511,9 +507,7 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
       for (int w = 1; w < 8; ++w) bmax = fmaxf(bmax, red[w][tok]);
       const int ex = pow2_scale_exp(bmax);
       const size_t row = (size_t)(off_e + m0 + tok);
-      uint32_t word = 0;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) word |= e4m3_rne(ldexpf(h[m][v], -ex)) << (8 * v);
+      const uint32_t word = e4m3x4_exp(h[m], ex);
       *reinterpret_cast<uint32_t*>(p.hq + row * N + n0 + 16 * wv + 4 * grp) = word;
       if (wv == 0 && grp == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
     }

@@ -40,8 +40,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float silu_w4(float g) { return g / (1.0f + expf(-g)); }
-
 // D = A . B with E8M0 block scales sa (A) and sb (B), from zero.  The asm
 // leaves 2 wait states between the VALU instructions that build the
 // operands and the MFMA (the compiler cannot insert them in front of an asm;
@@ -286,9 +284,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
       amax[v] = 0.f;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const float g = fminf(fmaxf(acc[tt][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[tt + 2][v], -lim), lim);
-        const float hv = silu_w4(g) * u;
+        const float g = clamp_sym(acc[tt][v], lim);
+        const float u = clamp_sym(acc[tt + 2][v], lim);
+        const float hv = silu_fast(g) * u;
         h[tt][v] = hv;
         amax[v] = fmaxf(amax[v], fabsf(hv));
       }
@@ -310,7 +308,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
       const size_t row = (size_t)(off_e + m0 + tok);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        p.hq[row * N + n0 + 32 * wv + 16 * tt + col] = (uint8_t)e4m3_rne(ldexpf(h[tt][v], -ex));
+        p.hq[row * N + n0 + 32 * wv + 16 * tt + col] = (uint8_t)e4m3x1(ldexpf(h[tt][v], -ex));
       if (wv == 0 && col == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
     }
   } else {
@@ -493,9 +491,9 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float g = fminf(fmaxf(acc[0][m][v], -lim), lim);
-        const float u = fminf(fmaxf(acc[1][m][v], -lim), lim);
-        h[m][v] = silu_w4(g) * u;
+        const float g = clamp_sym(acc[0][m][v], lim);
+        const float u = clamp_sym(acc[1][m][v], lim);
+        h[m][v] = silu_fast(g) * u;
         float a = fabsf(h[m][v]);
 #pragma unroll
         for (int k = 1; k < 16; k <<= 1) a = fmaxf(a, __shfl_xor(a, k));
@@ -519,7 +517,7 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
         for (int w = 1; w < 8; ++w) bmax = fmaxf(bmax, red[w][tok]);
         const int ex = pow2_scale_exp(bmax);
         const size_t row = (size_t)(off_e + m0 + tok);
-        p.hq[row * N + n0 + 16 * wv + col] = (uint8_t)e4m3_rne(ldexpf(h[m][v], -ex));
+        p.hq[row * N + n0 + 16 * wv + col] = (uint8_t)e4m3x1(ldexpf(h[m][v], -ex));
         if (wv == 0 && col == 0) p.hs[row * (N / 128) + n0 / 128] = (uint8_t)(ex + 127);
       }
   } else {

@@ -51,6 +51,34 @@ __device__ __forceinline__ uint32_t e4m3_rne(float s) {
   return code | sign;
 }
 
+// E4M3FN codes of four floats with |x| <= 448 in bytes 0..3, by the gfx950
+// conversion instruction: round to nearest even, sign kept -- the same code
+// as e4m3_rne for every float of that range (compared exhaustively on the
+// device).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// ... of x[0..3] * 2^-ex (x a float[4] or a 4-vector)
+template <class V>
+__device__ __forceinline__ uint32_t e4m3x4_exp(const V& x, int ex) {
+  return e4m3x4(ldexpf(x[0], -ex), ldexpf(x[1], -ex), ldexpf(x[2], -ex), ldexpf(x[3], -ex));
+}
+__device__ __forceinline__ uint32_t e4m3x1(float a) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.f, 0, false) & 0xFFu;
+}
+
+// SwiGLU's gate, silu(g) = g / (1 + e^-g), in fp32 with the hardware
+// exponential and reciprocal (a few ulp; g -> -inf gives -0, g -> +inf g).
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// x clamped to [-lim, lim] (lim > 0, +inf allowed) in one instruction.
+__device__ __forceinline__ float clamp_sym(float x, float lim) {
+  return __builtin_amdgcn_fmed3f(x, -lim, lim);
+}
+
 // FP8 E4M3 quantization of the 128-element block blk of a bf16 array (one
 // power-of-two scale per block, smallest with amax <= 448 * 2^e): 16 lanes
 // (sub = 0..15, consecutive lanes of one wave) take 8 elements each.  Blocks
@@ -75,11 +103,8 @@ __device__ __forceinline__ void quant_act_block(const uint16_t* __restrict__ x, 
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const int e = pow2_scale_exp(amax);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= e4m3_rne(ldexpf(v[i], -e)) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= e4m3_rne(ldexpf(v[4 + i], -e)) << (8 * i);
+  const uint32_t lo = e4m3x4(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
+  const uint32_t hi = e4m3x4(ldexpf(v[4], -e), ldexpf(v[5], -e), ldexpf(v[6], -e), ldexpf(v[7], -e));
   if (live) {
     *reinterpret_cast<uint2*>(q + blk * 128 + sub * 8) = make_uint2(lo, hi);
     if (sub == 0) scale[blk] = (uint8_t)(e + 127);
@@ -92,6 +117,7 @@ __device__ __forceinline__ void quant_act_block(const uint16_t* __restrict__ x, 
 constexpr int kGemmThreads = 256;     // 4 waves
 constexpr int kG1Cols = 128;          // h columns per GEMM1 workgroup (one FP8 block)
 constexpr int kG2Rows = 256;          // output columns per GEMM2 workgroup
+constexpr int kMaxExperts = 512;      // largest expert count a configuration may have
 
 // ---------------------------------------------------------------------------
 // Launchers (return hipGetLastError() after enqueueing)

@@ -173,7 +173,9 @@ def _bounds(inp, xq, xs, r, ref, wl, deq=quant.mxfp4_dequant, tau=None):
         bg, bu = tau * (np.abs(xd) @ np.abs(W1).T), tau * (np.abs(xd) @ np.abs(W3).T)
         gc, uc = np.clip(g, -lim, lim), np.clip(u, -lim, lim)
         dsilu = 1.1                                   # |d silu / dg| <= 1.0999
-        dh[lo:hi] = dsilu * np.abs(uc) * bg + np.abs(ffn.silu(gc)) * bu + 2.0 ** -23 * np.abs(ffn.silu(gc) * uc)
+        # h in fp32: silu with the hardware exponential and reciprocal (a few
+        # ulp, below 2^-19 relative for |g| <= 10) times u, one more rounding
+        dh[lo:hi] = dsilu * np.abs(uc) * bg + np.abs(ffn.silu(gc)) * bu + 2.0 ** -18 * np.abs(ffn.silu(gc) * uc)
         absw2[e] = np.abs(deq(inp["w2"][e], inp["w2_scale"][e]))
     return dh, absw2
 

@@ -9,10 +9,10 @@ builds the GEMM source for gfx950 and checks, in the generated AMD assembly,
 that no VALU instruction writes a scale register or the accumulator of a
 scaled MFMA within 32 wait states of it, and that nothing but another MFMA
 reads an MFMA's accumulator within that distance.  Before the MFMA, the
-hardware needs wait states between a VALU write of a source register (A, B
-or a scale) and the MFMA's read of it -- the compiler puts two there for the
-builtin -- which it cannot insert in front of an asm MFMA either: the check
-asks for at least PRE wait states there.  (A W4AFP8 GEMM whose B operand was
+hardware needs wait states between a VALU write of a source register (A, B,
+the accumulator or a scale) and the MFMA's read of it -- the compiler puts
+two there for the builtin -- which it cannot insert in front of an asm MFMA
+either: the check asks for at least PRE wait states there.  (A W4AFP8 GEMM whose B operand was
 written by the VALU instruction right before the asm MFMA read a stale value
 on gfx950.)  CPU-only: hipcc cross-compiles."""
 
@@ -83,7 +83,7 @@ def test_scaled_mfma_sources_settled_before_issue(src):
                 continue
             total += 1
             ops = [o.strip() for o in s.split(None, 1)[1].split(" op_sel")[0].split(",")]
-            srcs = _regs(ops[1]) | _regs(ops[2]) | _regs(ops[4]) | _regs(ops[5])
+            srcs = _regs(ops[1]) | _regs(ops[2]) | _regs(ops[3]) | _regs(ops[4]) | _regs(ops[5])
             ws = 0
             for t in reversed(ins[:i]):
                 if ws >= PRE:
