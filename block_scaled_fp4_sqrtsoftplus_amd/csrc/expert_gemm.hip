@@ -759,15 +759,36 @@ __device__ __forceinline__ int tile_slot(int t, int c) { return c ^ (t & 7); }
 
 constexpr int kTileBuf = 128 * 128;   // bytes of one activation buffer
 
-#define TILE_MFMA8                                                                                 \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %[a0], %[b0], %0, %[s0], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %[a1], %[b0], %1, %[s1], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %[a2], %[b0], %2, %[s2], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %[a3], %[b0], %3, %[s3], %[t0] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %[a0], %[b1], %4, %[s0], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %[a1], %[b1], %5, %[s1], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %[a2], %[b1], %6, %[s2], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %[a3], %[b1], %7, %[s3], %[t1] op_sel_hi:[0,0,0] cbsz:4\n\t"
+// Scale operands: one dword per token sub-tile (bytes = the four K steps of
+// a group) and one per weight tile (the lane's K block of those four steps,
+// see the transposed scale-line layout in the kernel).  The MFMA takes byte
+// Q of both: op_sel (low bit) and op_sel_hi (high bit) select the byte of
+// each scale operand (measured on gfx950).
+#define TILE_OPSEL_0 "op_sel:[0,0,0] op_sel_hi:[0,0,0]"
+#define TILE_OPSEL_1 "op_sel:[1,1,0] op_sel_hi:[0,0,0]"
+#define TILE_OPSEL_2 "op_sel:[0,0,0] op_sel_hi:[1,1,0]"
+#define TILE_OPSEL_3 "op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+#define TILE_MFMA(C, A, B, S, T, OPS)                                                         \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C "], %[" A "], %[" B "], %[" C "], %[" S "], %[" T \
+  "] " OPS " cbsz:4\n\t"
+#define TILE_MFMA4(C0, C1, C2, C3, B, T, OPS)                                                 \
+  TILE_MFMA(C0, "a0", B, "s0", T, OPS) TILE_MFMA(C1, "a1", B, "s1", T, OPS)                   \
+  TILE_MFMA(C2, "a2", B, "s2", T, OPS) TILE_MFMA(C3, "a3", B, "s3", T, OPS)
+// the asm statement BODY(op_sel of step Q) with outputs OUTS, inputs INS
+#define TILE_Q_ASM(BODY, OUTS, INS)                                 \
+  if constexpr (Q == 0) asm volatile(BODY(TILE_OPSEL_0) : OUTS : INS); \
+  else if constexpr (Q == 1) asm volatile(BODY(TILE_OPSEL_1) : OUTS : INS); \
+  else if constexpr (Q == 2) asm volatile(BODY(TILE_OPSEL_2) : OUTS : INS); \
+  else asm volatile(BODY(TILE_OPSEL_3) : OUTS : INS)
+
+#define TILE_ACC_OUT                                                                        \
+  [c0] "+a"(c0[0]), [c1] "+a"(c0[1]), [c2] "+a"(c0[2]), [c3] "+a"(c0[3]), [d0] "+a"(c1[0]), \
+      [d1] "+a"(c1[1]), [d2] "+a"(c1[2]), [d3] "+a"(c1[3]), [x0] "=&v"(x0), [x1] "=&v"(x1), \
+      [y0] "=&v"(y0), [y1] "=&v"(y1)
+#define TILE_OPND_IN                                                                         \
+  [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0), [b1] "v"(b1), \
+      [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]), [lo] "v"(lo),       \
+      [hi] "v"(hi)
 
 // Activations of two sub-tiles (tokens 16*m + col and 16*(m+1) + col) of the
 // buffer at byte offset BOFF: operand b = {chunk grp, chunk 4 + grp}.
@@ -786,63 +807,36 @@ __device__ __forceinline__ void tile_read2(v8i& b0, v8i& b1, uint32_t lo, uint32
   b1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 }
 
-// 8 MFMAs on (b0, b1) while reading the next two sub-tiles at OFF into
-// (n0, n1); the block ends once the reads have landed and 32 wait states
-// have passed since the last MFMA.
-// 8 MFMAs on (b0, b1) while reading the next two sub-tiles at OFF into
-// (n0, n1); the block ends once the reads have landed.  No wait states: the
-// caller keeps the scale registers and accumulators untouched until the
-// step's last block, which closes with them.
-template <int OFF>
+// 8 MFMAs of step Q on (b0, b1) -- two token sub-tiles x four weight tiles --
+// while reading the next two sub-tiles at OFF into (n0, n1); the block ends
+// once the reads have landed.  No wait states: the caller keeps the scale
+// registers and accumulators untouched until the step's last block, which
+// closes with them.
+#define TILE_READ_BODY(OPS)                                                         \
+  "ds_read_b128 %[x0], %[lo] offset:%[o0]\n\t"                                      \
+  "ds_read_b128 %[x1], %[hi] offset:%[o0]\n\t"                                      \
+  "ds_read_b128 %[y0], %[lo] offset:%[o1]\n\t"                                      \
+  "ds_read_b128 %[y1], %[hi] offset:%[o1]\n\t"                                      \
+  TILE_MFMA4("c0", "c1", "c2", "c3", "b0", "t0", OPS)                               \
+  TILE_MFMA4("d0", "d1", "d2", "d3", "b1", "t1", OPS) "s_waitcnt lgkmcnt(0)"
+#define TILE_READ_IN TILE_OPND_IN, [t0] "v"(sb0), [t1] "v"(sb1), [o0] "n"(OFF), [o1] "n"(OFF + 2048)
+template <int OFF, int Q>
 __device__ __forceinline__ void tile_mfma8_read(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
                                                 const v8i& b0, const v8i& b1, const int (&sa)[4],
                                                 int sb0, int sb1, v8i& n0, v8i& n1, uint32_t lo,
                                                 uint32_t hi) {
   v4i x0, x1, y0, y1;
-  asm volatile(
-      "ds_read_b128 %[x0], %[lo] offset:%[o0]\n\t"
-      "ds_read_b128 %[x1], %[hi] offset:%[o0]\n\t"
-      "ds_read_b128 %[y0], %[lo] offset:%[o1]\n\t"
-      "ds_read_b128 %[y1], %[hi] offset:%[o1]\n\t"
-      TILE_MFMA8
-      "s_waitcnt lgkmcnt(0)"
-      : "+a"(c0[0]), "+a"(c0[1]), "+a"(c0[2]), "+a"(c0[3]),
-        "+a"(c1[0]), "+a"(c1[1]), "+a"(c1[2]), "+a"(c1[3]),
-        [x0] "=&v"(x0), [x1] "=&v"(x1), [y0] "=&v"(y0), [y1] "=&v"(y1)
-      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0),
-        [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]),
-        [t0] "v"(sb0), [t1] "v"(sb1), [lo] "v"(lo), [hi] "v"(hi), [o0] "n"(OFF),
-        [o1] "n"(OFF + 2048));
+  TILE_Q_ASM(TILE_READ_BODY, TILE_ACC_OUT, TILE_READ_IN);
   n0 = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   n1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 }
 
-// The last 8 MFMAs of a step (sub-tiles 6, 7), closed by 32 wait states.
-// Also takes the step's other token scale registers (sb[0..5]) and the
-// previous block's activation operands (p0, p1), so that none of them is
-// reused before those wait states have passed.
-__device__ __forceinline__ void tile_mfma8_last(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
-                                                const v8i& b0, const v8i& b1, const int (&sa)[4],
-                                                const int (&sb)[8], const v8i& p0, const v8i& p1) {
-  asm volatile(
-      TILE_MFMA8
-      "s_nop 15\n\t"
-      "s_nop 15"
-      : "+a"(c0[0]), "+a"(c0[1]), "+a"(c0[2]), "+a"(c0[3]),
-        "+a"(c1[0]), "+a"(c1[1]), "+a"(c1[2]), "+a"(c1[3])
-      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0),
-        [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]),
-        [t0] "v"(sb[6]), [t1] "v"(sb[7]), [k0] "v"(sb[0]), [k1] "v"(sb[1]), [k2] "v"(sb[2]),
-        [k3] "v"(sb[3]), [k4] "v"(sb[4]), [k5] "v"(sb[5]), [p0] "v"(p0), [p1] "v"(p1));
-}
-#undef TILE_MFMA8
-
 // Scales of a group of four K steps: the token scale dwords of the 8
 // sub-tiles (bytes s..s+3 of token 16*m + col's line: tok + m * TROW) and
-// the weight scale bytes 4s..4s+15 of the lane's row in each of the four
-// weight tiles (wrow + t * WROW).
+// the weight scale dwords of the lane's row in each of the four weight tiles
+// (wrow + t * WROW; the lane's K block, steps s..s+3).
 template <int TROW, int WROW>
-__device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4], uint32_t tok,
+__device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], uint32_t (&ww)[4], uint32_t tok,
                                                  uint32_t wrow) {
   asm volatile(
       "ds_read_b32 %0, %12\n\t"
@@ -853,10 +847,10 @@ __device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4]
       "ds_read_b32 %5, %12 offset:%18\n\t"
       "ds_read_b32 %6, %12 offset:%19\n\t"
       "ds_read_b32 %7, %12 offset:%20\n\t"
-      "ds_read_b128 %8, %13\n\t"
-      "ds_read_b128 %9, %13 offset:%21\n\t"
-      "ds_read_b128 %10, %13 offset:%22\n\t"
-      "ds_read_b128 %11, %13 offset:%23\n\t"
+      "ds_read_b32 %8, %13\n\t"
+      "ds_read_b32 %9, %13 offset:%21\n\t"
+      "ds_read_b32 %10, %13 offset:%22\n\t"
+      "ds_read_b32 %11, %13 offset:%23\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(tw[0]), "=&v"(tw[1]), "=&v"(tw[2]), "=&v"(tw[3]), "=&v"(tw[4]), "=&v"(tw[5]),
         "=&v"(tw[6]), "=&v"(tw[7]), "=&v"(ww[0]), "=&v"(ww[1]), "=&v"(ww[2]), "=&v"(ww[3])
@@ -864,18 +858,14 @@ __device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4]
         "n"(5 * TROW), "n"(6 * TROW), "n"(7 * TROW), "n"(WROW), "n"(2 * WROW), "n"(3 * WROW));
 }
 
-// The last 8 MFMAs of a step (sub-tiles 6, 7) with the next step's LDS work
+// The last 8 MFMAs of step Q (sub-tiles 6, 7) with the next step's LDS work
 // in their shadow: after the first four, the reads of the next step's first
 // two sub-tiles (buffer offset OFFN) into n0, n1, and the LDS stores of this
 // thread's staged activation registers r (at wa + WOFF + 1024 * j); with SC
-// also the next group's scale lines, as tile_read_scales (into tw, ww).
+// also the next group's scales, as tile_read_scales (into tw, ww, registers
+// of their own: the MFMAs after the reads still use the current ones).
 // Every scale register of the step is an input, so that none is reused
 // before the closing 32 wait states; then the LDS wait.
-#define TILE_LAST_MFMA4(C0, C1, C2, C3, B, T)                                                 \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C0 "], %[a0], %[" B "], %[" C0 "], %[s0], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C1 "], %[a1], %[" B "], %[" C1 "], %[s1], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C2 "], %[a2], %[" B "], %[" C2 "], %[s2], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C3 "], %[a3], %[" B "], %[" C3 "], %[s3], %[" T "] op_sel_hi:[0,0,0] cbsz:4\n\t"
 #define TILE_LAST_LDS                                \
   "ds_read_b128 %[x0], %[lo] offset:%[o0]\n\t"       \
   "ds_read_b128 %[x1], %[hi] offset:%[o0]\n\t"       \
@@ -894,66 +884,69 @@ __device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], v4i (&ww)[4]
   "ds_read_b32 %[tw5], %[tok] offset:%[q5]\n\t"       \
   "ds_read_b32 %[tw6], %[tok] offset:%[q6]\n\t"       \
   "ds_read_b32 %[tw7], %[tok] offset:%[q7]\n\t"       \
-  "ds_read_b128 %[ww0], %[wrow]\n\t"                  \
-  "ds_read_b128 %[ww1], %[wrow] offset:%[p1]\n\t"     \
-  "ds_read_b128 %[ww2], %[wrow] offset:%[p2]\n\t"     \
-  "ds_read_b128 %[ww3], %[wrow] offset:%[p3]\n\t"
+  "ds_read_b32 %[ww0], %[wrow]\n\t"                   \
+  "ds_read_b32 %[ww1], %[wrow] offset:%[p1]\n\t"      \
+  "ds_read_b32 %[ww2], %[wrow] offset:%[p2]\n\t"      \
+  "ds_read_b32 %[ww3], %[wrow] offset:%[p3]\n\t"
 #define TILE_LAST_CLOSE "s_nop 15\n\ts_nop 15\n\ts_waitcnt lgkmcnt(0)"
-#define TILE_LAST_OUT                                                                          \
-  [c0] "+a"(c0[0]), [c1] "+a"(c0[1]), [c2] "+a"(c0[2]), [c3] "+a"(c0[3]), [d0] "+a"(c1[0]),    \
-      [d1] "+a"(c1[1]), [d2] "+a"(c1[2]), [d3] "+a"(c1[3]), [x0] "=&v"(x0), [x1] "=&v"(x1),    \
-      [y0] "=&v"(y0), [y1] "=&v"(y1)
+#define TILE_LAST_BODY(OPS)                                              \
+  "s_nop 1\n\t" TILE_MFMA4("c0", "c1", "c2", "c3", "b0", "t6", OPS)       \
+  TILE_LAST_LDS TILE_MFMA4("d0", "d1", "d2", "d3", "b1", "t7", OPS) TILE_LAST_CLOSE
+#define TILE_LAST_SC_BODY(OPS)                                           \
+  "s_nop 1\n\t" TILE_MFMA4("c0", "c1", "c2", "c3", "b0", "t6", OPS)       \
+  TILE_LAST_LDS TILE_LAST_SCALES                                         \
+  TILE_MFMA4("d0", "d1", "d2", "d3", "b1", "t7", OPS) TILE_LAST_CLOSE
 #define TILE_LAST_IN                                                                           \
-  [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b0), [b1] "v"(b1),  \
-      [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]), [s3] "v"(sa[3]), [t6] "v"(sb[6]),     \
-      [t7] "v"(sb[7]), [k0] "v"(sb[0]), [k1] "v"(sb[1]), [k2] "v"(sb[2]), [k3] "v"(sb[3]),     \
-      [k4] "v"(sb[4]), [k5] "v"(sb[5]), [lo] "v"(lo), [hi] "v"(hi), [o0] "n"(OFFN),            \
+  TILE_OPND_IN, [t6] "v"(sb[6]), [t7] "v"(sb[7]), [k0] "v"(sb[0]), [k1] "v"(sb[1]),            \
+      [k2] "v"(sb[2]), [k3] "v"(sb[3]), [k4] "v"(sb[4]), [k5] "v"(sb[5]), [o0] "n"(OFFN),      \
       [o1] "n"(OFFN + 2048), [wa] "v"(wa), [r0] "v"(r[0]), [r1] "v"(r[1]), [r2] "v"(r[2]),     \
       [r3] "v"(r[3]), [w0] "n"(WOFF), [w1] "n"(WOFF + 1024), [w2] "n"(WOFF + 2048),             \
       [w3] "n"(WOFF + 3072)
-template <int OFFN, int WOFF, bool SC, int TROW, int WROW>
+#define TILE_LAST_SC_OUT                                                                      \
+  TILE_ACC_OUT, [tw0] "=&v"(tw[0]), [tw1] "=&v"(tw[1]), [tw2] "=&v"(tw[2]), [tw3] "=&v"(tw[3]), \
+      [tw4] "=&v"(tw[4]), [tw5] "=&v"(tw[5]), [tw6] "=&v"(tw[6]), [tw7] "=&v"(tw[7]),         \
+      [ww0] "=&v"(ww[0]), [ww1] "=&v"(ww[1]), [ww2] "=&v"(ww[2]), [ww3] "=&v"(ww[3])
+#define TILE_LAST_SC_IN                                                                    \
+  TILE_LAST_IN, [tok] "v"(tok), [wrow] "v"(wrow), [q1] "n"(TROW), [q2] "n"(2 * TROW),      \
+      [q3] "n"(3 * TROW), [q4] "n"(4 * TROW), [q5] "n"(5 * TROW), [q6] "n"(6 * TROW),      \
+      [q7] "n"(7 * TROW), [p1] "n"(WROW), [p2] "n"(2 * WROW), [p3] "n"(3 * WROW)
+template <int OFFN, int WOFF, bool SC, int TROW, int WROW, int Q>
 __device__ __forceinline__ void tile_mfma8_last_pf(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
                                                    const v8i& b0, const v8i& b1,
                                                    const int (&sa)[4], const int (&sb)[8],
                                                    v8i& n0, v8i& n1, uint32_t lo, uint32_t hi,
                                                    const v4i (&r)[4], uint32_t wa,
-                                                   uint32_t (&tw)[8], v4i (&ww)[4], uint32_t tok,
-                                                   uint32_t wrow) {
+                                                   uint32_t (&tw)[8], uint32_t (&ww)[4],
+                                                   uint32_t tok, uint32_t wrow) {
   v4i x0, x1, y0, y1;
   if constexpr (SC) {
-    asm volatile("s_nop 1\n\t"
-                 TILE_LAST_MFMA4("c0", "c1", "c2", "c3", "b0", "t6")
-                 TILE_LAST_LDS
-                 TILE_LAST_SCALES
-                 TILE_LAST_MFMA4("d0", "d1", "d2", "d3", "b1", "t7")
-                 TILE_LAST_CLOSE
-                 : TILE_LAST_OUT, [tw0] "=&v"(tw[0]), [tw1] "=&v"(tw[1]), [tw2] "=&v"(tw[2]),
-                   [tw3] "=&v"(tw[3]), [tw4] "=&v"(tw[4]), [tw5] "=&v"(tw[5]), [tw6] "=&v"(tw[6]),
-                   [tw7] "=&v"(tw[7]), [ww0] "=&v"(ww[0]), [ww1] "=&v"(ww[1]), [ww2] "=&v"(ww[2]),
-                   [ww3] "=&v"(ww[3])
-                 : TILE_LAST_IN, [tok] "v"(tok), [wrow] "v"(wrow), [q1] "n"(TROW),
-                   [q2] "n"(2 * TROW), [q3] "n"(3 * TROW), [q4] "n"(4 * TROW), [q5] "n"(5 * TROW),
-                   [q6] "n"(6 * TROW), [q7] "n"(7 * TROW), [p1] "n"(WROW), [p2] "n"(2 * WROW),
-                   [p3] "n"(3 * WROW));
+    TILE_Q_ASM(TILE_LAST_SC_BODY, TILE_LAST_SC_OUT, TILE_LAST_SC_IN);
   } else {
-    asm volatile("s_nop 1\n\t"
-                 TILE_LAST_MFMA4("c0", "c1", "c2", "c3", "b0", "t6")
-                 TILE_LAST_LDS
-                 TILE_LAST_MFMA4("d0", "d1", "d2", "d3", "b1", "t7")
-                 TILE_LAST_CLOSE
-                 : TILE_LAST_OUT
-                 : TILE_LAST_IN);
+    TILE_Q_ASM(TILE_LAST_BODY, TILE_ACC_OUT, TILE_LAST_IN);
     (void)tw; (void)ww; (void)tok; (void)wrow;
   }
   n0 = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   n1 = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 }
-#undef TILE_LAST_MFMA4
 #undef TILE_LAST_LDS
 #undef TILE_LAST_SCALES
 #undef TILE_LAST_CLOSE
-#undef TILE_LAST_OUT
+#undef TILE_LAST_BODY
+#undef TILE_LAST_SC_BODY
 #undef TILE_LAST_IN
+#undef TILE_LAST_SC_OUT
+#undef TILE_LAST_SC_IN
+#undef TILE_READ_BODY
+#undef TILE_READ_IN
+#undef TILE_ACC_OUT
+#undef TILE_OPND_IN
+#undef TILE_Q_ASM
+#undef TILE_MFMA4
+#undef TILE_MFMA
+#undef TILE_OPSEL_0
+#undef TILE_OPSEL_1
+#undef TILE_OPSEL_2
+#undef TILE_OPSEL_3
 
 // Workgroup barrier once this wave's LDS writes are done; no memory access
 // is moved across it (outstanding global loads stay in flight).
@@ -1078,7 +1071,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     return live;
   };
   const uint32_t wlo = (uint32_t)(col * (K / 2) + 16 * grp);
-  const uint32_t slo = (uint32_t)(col * (K / 32) + S * grp);
 
   // activation staging: this thread moves 4 x 16 bytes per step, for tile
   // tokens 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the
@@ -1105,22 +1097,47 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     for (int t = 0; t < 4; ++t) a[t] = gload<v4i>(wb[t] + wlo + s * 64);
   };
 
-  // Scale lines: thread (wv, lane) copies bytes S*grp .. S*grp + S - 1 of the
-  // line of row 16*t + col of its wave (t = 0..3) and half of the token scale
-  // line of tile token tid/2.
-  typedef typename std::conditional<S == 8, v2i, v4i>::type SChunk;
-  constexpr int SN = S == 8 ? 1 : S / 16;
-  struct WLine { SChunk c[SN]; };
-  auto wline_load = [&](const uint8_t* src) {
+  // Weight scale lines in LDS, transposed per group of four K steps: the
+  // line's 16 bytes of steps 4g..4g+3 (byte 4*q + kb: step q, K block kb)
+  // are stored as byte 4*kb + q, so that the lane of K block grp reads the
+  // four steps' scales of its block as one dword (the MFMA's op_sel then
+  // picks the step's byte).  Thread (wv, lane) copies the 16-byte groups
+  // L = 4*i + grp (i = 0 .. NG-1) of the wave's 64 row lines (NG groups
+  // each): row 16*(L / NG) + col, group L % NG.
+  constexpr int NG = S / 4;                 // 16-byte groups per line
+  constexpr int CPS = NG >= 4 ? NG / 4 : 1;  // groups a thread copies per preparation step
+  struct WLine { v4i c[CPS]; };
+  auto sel4 = [](const uint8_t* const (&b)[4], int t) {
+    return t == 0 ? b[0] : t == 1 ? b[1] : t == 2 ? b[2] : b[3];
+  };
+  auto wgroup_src = [&](const uint8_t* const (&sbp)[4], int i) {
+    const int L = 4 * i + grp;
+    return sel4(sbp, L / NG) + col * (K / 32) + 16 * (L % NG);
+  };
+  auto wline_load = [&](const uint8_t* const (&sbp)[4], int i0) {
     WLine w;
 #pragma unroll
-    for (int k = 0; k < SN; ++k) w.c[k] = gload<SChunk>(src + slo + k * sizeof(SChunk));
+    for (int k = 0; k < CPS; ++k) w.c[k] = i0 + k < NG ? gload<v4i>(wgroup_src(sbp, i0 + k)) : v4i{0, 0, 0, 0};
     return w;
   };
-  auto wline_store = [&](int b, int t, const WLine& w) {
+  // 4x4 byte transpose of a 16-byte group (dword q, byte kb -> dword kb, byte q)
+  auto transpose16 = [](const v4i& d) {
+    const uint32_t lo01 = __builtin_amdgcn_perm((uint32_t)d[1], (uint32_t)d[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm((uint32_t)d[1], (uint32_t)d[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm((uint32_t)d[3], (uint32_t)d[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm((uint32_t)d[3], (uint32_t)d[2], 0x07030602u);
+    return v4i{(int)__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+               (int)__builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+               (int)__builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+               (int)__builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+  };
+  auto wline_store = [&](int b, int i0, const WLine& w) {
 #pragma unroll
-    for (int k = 0; k < SN; ++k)
-      reinterpret_cast<SChunk*>(&wsc[b][wv][16 * t + col][S * grp])[k] = w.c[k];
+    for (int k = 0; k < CPS; ++k) {
+      if (i0 + k >= NG) break;
+      const int L = 4 * (i0 + k) + grp;
+      *reinterpret_cast<v4i*>(&wsc[b][wv][16 * (L / NG) + col][16 * (L % NG)]) = transpose16(w.c[k]);
+    }
   };
   typedef typename std::conditional<S == 32, v4i, typename std::conditional<S == 16, v2i, int>::type>::type TChunk;
   auto tline_src = [&](int row) { return p.a_scale + (size_t)row * S + (tid & 1) * (S / 2); };
@@ -1150,7 +1167,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     for (int j = 0; j < 4; ++j) ssrc[j] = p.a + (size_t)rows[j] * K + 16 * a_slot;
     tline_store(0, gload<TChunk>(tline_src(srow)));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wline_store(0, t, wline_load(sb[t]));
+    for (int i0 = 0; i0 < NG; i0 += CPS) wline_store(0, i0, wline_load(sb, i0));
   }
 
   v4f acc[MT][4];
@@ -1178,12 +1195,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   const uint32_t rd_lo = lds_addr(act) + col * 128 + 16 * rslot;
   const uint32_t rd_hi = rd_lo ^ 64u;
   const uint32_t st_wa = lds_addr(act) + sdst;
-  uint32_t sbw[MT];
-  v4i saw[4];
+  uint32_t sbw[MT];  // token scales of the group's four steps, per sub-tile
+  uint32_t saw[4];   // weight scales of the lane's K block for those steps, per weight tile
   v8i x0, x1;
   lds_barrier();
   tile_read_scales<16 * S, 16 * WLINE>(sbw, saw, lds_addr(&bsc[0][col][0]),
-                                       lds_addr(&wsc[0][wv][col][0]));
+                                       lds_addr(&wsc[0][wv][col][4 * grp]));
   tile_read2<0>(x0, x1, rd_lo, rd_hi);
 
   using I0 = std::integral_constant<int, 0>;
@@ -1194,10 +1211,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   for (int jt = 0; jt < n_my; ++jt) {
     const int cb = jt & 1, nb = cb ^ 1;  // scale buffers of this and the next tile
     const uint32_t sc_tok = lds_addr(&bsc[cb][col][0]);
-    const uint32_t sc_w = lds_addr(&wsc[cb][wv][col][0]);
+    const uint32_t sc_w = lds_addr(&wsc[cb][wv][col][4 * grp]);
 
     const uint32_t nsc_tok = lds_addr(&bsc[nb][col][0]);
-    const uint32_t nsc_w = lds_addr(&wsc[nb][wv][col][0]);
+    const uint32_t nsc_w = lds_addr(&wsc[nb][wv][col][4 * grp]);
 
     // One K step from buffer Q (compile-time) and ring slot Q; its operands
     // for sub-tiles 0, 1 (x0, x1) and, at Q == 0, the group's scales were
@@ -1212,26 +1229,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         stage_store((Q + 2) & 3, R2[Q & 1]);
         return;
       }
-      const int sa[4] = {saw[0][Q] >> (8 * grp), saw[1][Q] >> (8 * grp), saw[2][Q] >> (8 * grp),
-                         saw[3][Q] >> (8 * grp)};
-      const int sh = 8 * Q;
-      const int sbv[8] = {(int)(sbw[0] >> sh), (int)(sbw[1] >> sh), (int)(sbw[2] >> sh),
-                          (int)(sbw[3] >> sh), (int)(sbw[4] >> sh), (int)(sbw[5] >> sh),
-                          (int)(sbw[6] >> sh), (int)(sbw[7] >> sh)};
+      // the MFMAs take byte Q of these (op_sel)
+      const int sa[4] = {(int)saw[0], (int)saw[1], (int)saw[2], (int)saw[3]};
+      const int sbv[8] = {(int)sbw[0], (int)sbw[1], (int)sbw[2], (int)sbw[3],
+                          (int)sbw[4], (int)sbw[5], (int)sbw[6], (int)sbw[7]};
       constexpr int B = Q * kTileBuf;
       constexpr int BN = ((Q + 1) & 3) * kTileBuf;
       v8i y0, y1;
       // one guard per step: every scale register of the step stays live
       // until the last block, which closes with the wait states
-      tile_mfma8_read<B + 2 * 2048>(acc[0], acc[1], A[Q], x0, x1, sa, sbv[0], sbv[1], y0, y1,
+      tile_mfma8_read<B + 2 * 2048, Q>(acc[0], acc[1], A[Q], x0, x1, sa, sbv[0], sbv[1], y0, y1,
                                     rd_lo, rd_hi);
-      tile_mfma8_read<B + 4 * 2048>(acc[2], acc[3], A[Q], y0, y1, sa, sbv[2], sbv[3], x0, x1,
+      tile_mfma8_read<B + 4 * 2048, Q>(acc[2], acc[3], A[Q], y0, y1, sa, sbv[2], sbv[3], x0, x1,
                                     rd_lo, rd_hi);
-      tile_mfma8_read<B + 6 * 2048>(acc[4], acc[5], A[Q], x0, x1, sa, sbv[4], sbv[5], y0, y1,
+      tile_mfma8_read<B + 6 * 2048, Q>(acc[4], acc[5], A[Q], x0, x1, sa, sbv[4], sbv[5], y0, y1,
                                     rd_lo, rd_hi);
       const uint32_t tok = LAST ? nsc_tok : sc_tok + s + 1;
       const uint32_t wrow = LAST ? nsc_w : sc_w + 4 * (s + 1);
-      tile_mfma8_last_pf<BN, WB, Q == 3, 16 * S, 16 * WLINE>(acc[6], acc[7], A[Q], y0, y1, sa,
+      tile_mfma8_last_pf<BN, WB, Q == 3, 16 * S, 16 * WLINE, Q>(acc[6], acc[7], A[Q], y0, y1, sa,
                                                              sbv, x0, x1, rd_lo, rd_hi,
                                                              R2[Q & 1], st_wa, sbw, saw, tok,
                                                              wrow);
@@ -1262,7 +1277,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         const int ps = pair_slot(nxt, tid >> 1);
         nraw_s = MODE == 1 ? gload<int>(p.sorted_pairs + ps) : ps;
       } else if constexpr (P >= 1 && P <= 4) {
-        wtmp[(P - 1) & 1] = wline_load(nsb[P - 1]);
+        wtmp[(P - 1) & 1] = wline_load(nsb, (P - 1) * CPS);
         if constexpr (P == 4) {
           ttmp = gload<TChunk>(tline_src(MODE == 1 ? nraw_s / p.top_k : nraw_s));
 #pragma unroll
@@ -1273,7 +1288,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     };
     auto prep_store = [&](auto pc) {
       constexpr int P = decltype(pc)::value;
-      if constexpr (P >= 2 && P <= 5) wline_store(nb, P - 2, wtmp[P & 1]);
+      if constexpr (P >= 2 && P <= 5) wline_store(nb, (P - 2) * CPS, wtmp[P & 1]);
       if constexpr (P == 5) tline_store(nb, ttmp);
     };
 
