@@ -249,18 +249,32 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(int32_t* __restrict__ co
                                                         int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int32_t tot[512];
   const int e = threadIdx.x;
+  // the chunk column of expert e in batches of 16 independent loads (one
+  // dependent load per chunk would make the kernel latency-bound)
+  constexpr int NB = 16;
   int32_t sum = 0;
   if (e < E)
-    for (int c = 0; c < chunks; ++c) sum += counts[(size_t)c * E + e];
+    for (int c0 = 0; c0 < chunks; c0 += NB) {
+      int32_t v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[j] = c0 + j < chunks ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sum += v[j];
+    }
   const int32_t incl = block_scan512(tot, sum);
   if (e < E) {
     int32_t base = incl - sum;  // exclusive
     offsets[e] = base;
     if (e == E - 1) offsets[E] = incl;
-    for (int c = 0; c < chunks; ++c) {
-      const int32_t n = counts[(size_t)c * E + e];
-      counts[(size_t)c * E + e] = base;
-      base += n;
+    for (int c0 = 0; c0 < chunks; c0 += NB) {
+      int32_t v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[j] = c0 + j < chunks ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (c0 + j < chunks) counts[(size_t)(c0 + j) * E + e] = base;
+        base += v[j];
+      }
     }
   }
   if (mtile_off) {
