@@ -370,8 +370,10 @@ __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __re
 // step line with its 16-byte chunk c at slot c ^ (row & 7), so that the
 // 16-byte operand reads of 16 consecutive rows hit distinct banks); the four
 // waves split the tile 2 x 2 (64 tokens x 64 rows each, 32 MFMAs per step).
-// The next step's lines are loaded into registers at the start of a step
-// and written to the other buffer at its end; one barrier per step.
+// Lines are loaded into registers two steps ahead (two register sets, the
+// K loop unrolled by two so that the set is a compile-time choice: 3-6%
+// over one step ahead) and written to the other buffer at the end of the
+// step before theirs; one barrier per step.
 //   EPI_F32    rows n0..n0+127 of W, out[t][n] fp32
 //   EPI_SWIGLU LDS rows 0..63 = w1 rows c0..c0+63, rows 64..127 = w3 rows of
 //              the same columns; wave (wm, wn) takes columns c0 + 32 wn ..
@@ -424,19 +426,22 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
     soff[j] = r * kBfTileLine + 16 * (sc ^ (r & 7));
   }
   // (native vector types: loops of struct copies would go through memory)
-  v4i ga[4], gb[4];
-  auto gload = [&](int s) {
+  // two staging sets: step s's lines in set s & 1, loaded two steps ahead
+  v4i ga[2][4], gb[2][4];
+  auto gload = [&](int s, auto setc) {
+    constexpr int SET = decltype(setc)::value;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ga[j] = *reinterpret_cast<const v4i*>(wsrc[j] + (size_t)s * kBfTileLine);
-      gb[j] = *reinterpret_cast<const v4i*>(xsrc[j] + (size_t)s * kBfTileLine);
+      ga[SET][j] = *reinterpret_cast<const v4i*>(wsrc[j] + (size_t)s * kBfTileLine);
+      gb[SET][j] = *reinterpret_cast<const v4i*>(xsrc[j] + (size_t)s * kBfTileLine);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](auto bufc) {   // buffer BUF from set BUF
+    constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<v4i*>(&As[buf][soff[j]]) = ga[j];
-      *reinterpret_cast<v4i*>(&Bs[buf][soff[j]]) = gb[j];
+      *reinterpret_cast<v4i*>(&As[BUF][soff[j]]) = ga[BUF][j];
+      *reinterpret_cast<v4i*>(&Bs[BUF][soff[j]]) = gb[BUF][j];
     }
   };
 
@@ -455,23 +460,27 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
   const int steps = kc / 64;
-  gload(0);
-  lstore(0);
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    __syncthreads();                  // buffer buf written, buffer buf^1 free
-    if (s + 1 < steps) gload(s + 1);
+  // step s from buffer BUF = s & 1 (compile-time in the unrolled pair): the
+  // lines of step s + 2 are loaded into set BUF once step s's lines (that
+  // set) are in LDS, and step s + 1's (set BUF ^ 1) are written to the other
+  // buffer at the end
+  auto step = [&](int s, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    __syncthreads();                  // buffer BUF written, buffer BUF^1 free
+    if (s + 2 < steps) gload(s + 2, bufc);
     bf16x8 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint8_t* r = &As[buf][(arow[t] + col) * kBfTileLine];
+      const uint8_t* r = &As[BUF][(arow[t] + col) * kBfTileLine];
       a0[t] = *reinterpret_cast<const bf16x8*>(r + lo);
       a1[t] = *reinterpret_cast<const bf16x8*>(r + hi);
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint8_t* r = &Bs[buf][(64 * wm + 16 * m + col) * kBfTileLine];
+      const uint8_t* r = &Bs[BUF][(64 * wm + 16 * m + col) * kBfTileLine];
       b0[m] = *reinterpret_cast<const bf16x8*>(r + lo);
       b1[m] = *reinterpret_cast<const bf16x8*>(r + hi);
     }
@@ -482,8 +491,17 @@ __global__ __launch_bounds__(256, 2) void bf16_tile_kernel(const uint16_t* __res
         acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[t], b0[m], acc[t][m], 0, 0, 0);
         acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[t], b1[m], acc[t][m], 0, 0, 0);
       }
-    if (s + 1 < steps) lstore(buf ^ 1);
+    if (s + 1 < steps) lstore(std::integral_constant<int, BUF ^ 1>{});
+  };
+  gload(0, C0{});
+  if (steps > 1) gload(1, C1{});
+  lstore(C0{});
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(s, C0{});
+    step(s + 1, C1{});
   }
+  if (s < steps) step(s, C0{});
 
   // D layout: lane l holds D[4*(l/16)+v][l%16] = C[token l%16][row 4*(l/16)+v]
 #pragma unroll
