@@ -8,28 +8,41 @@
 
 namespace moe {
 
+// K = k (compile-time): the k pair positions and weights, then all k rows'
+// float4 loads are issued before the first multiply-add, so a thread has
+// k + 1 row loads in flight instead of one at a time.
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ ysh,
-                                                      uint16_t* __restrict__ y, int64_t T, int H,
-                                                      int k) {
+                                                      uint16_t* __restrict__ y, int64_t T, int H) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of y
   const int per_row = H / 4;
   const int64_t t = q / per_row;
   if (t >= T) return;
   const int c = (int)(q - t * per_row) * 4;
+  int32_t pp[K];
+  float wj[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    pp[j] = pair_pos[t * K + j];
+    wj[j] = w[t * K + j];
+  }
+  float4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const float4*>(o + (size_t)pp[j] * H + c);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (ysh) s = *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)pair_pos[t * k + j] * H + c);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    acc.x = fmaf(wj[j], v[j].x, acc.x);
+    acc.y = fmaf(wj[j], v[j].y, acc.y);
+    acc.z = fmaf(wj[j], v[j].z, acc.z);
+    acc.w = fmaf(wj[j], v[j].w, acc.w);
   }
   if (ysh) {
-    const float4 s = *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c);
     acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
   }
   const uint32_t lo = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
@@ -42,8 +55,18 @@ hipError_t launch_combine(const float* o, const float* topk_w, const int32_t* pa
                           hipStream_t st) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, o,
-                     topk_w, pair_pos, ysh, y, T, H, k);
+  const dim3 grid((unsigned)((n + 255) / 256));
+#define MOE_COMBINE(KK)                                                                      \
+  case KK:                                                                                   \
+    hipLaunchKernelGGL((combine_kernel<KK>), grid, dim3(256), 0, st, o, topk_w, pair_pos, ysh, \
+                       y, T, H);                                                             \
+    break;
+  switch (k) {
+    MOE_COMBINE(1) MOE_COMBINE(2) MOE_COMBINE(3) MOE_COMBINE(4)
+    MOE_COMBINE(5) MOE_COMBINE(6) MOE_COMBINE(7) MOE_COMBINE(8)
+    default: return hipErrorInvalidValue;   // 1 <= k <= 8 is checked by the caller
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
