@@ -224,21 +224,25 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += 256) counts[c * E + e] = h[e];
 }
 
-// inclusive scan of one value per thread over a 512-thread workgroup
-// (Hillis-Steele in LDS)
-__device__ __forceinline__ int32_t block_scan512(int32_t* tot, int32_t v) {
-  const int e = threadIdx.x;
-  tot[e] = v;
-  __syncthreads();
-  for (int off = 1; off < 512; off <<= 1) {
-    const int32_t u = e >= off ? tot[e - off] : 0;
-    __syncthreads();
-    tot[e] += u;
-    __syncthreads();
+// inclusive scan of one value per thread over the first 512 threads of the
+// workgroup (threads past 512 take part in the barriers; their result is
+// meaningless): a shuffle scan inside each wave, then each wave adds the
+// totals of the waves below it -- two barriers (a Hillis-Steele scan in LDS
+// took eighteen).  wtot: 8 ints of LDS.
+__device__ __forceinline__ int32_t block_scan512(int32_t* wtot, int32_t v) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-  const int32_t r = tot[e];
+  if (lane == 63 && wv < 8) wtot[wv] = v;
   __syncthreads();
-  return r;
+  int32_t below = 0;
+  for (int w = 0; w < wv && w < 8; ++w) below += wtot[w];
+  __syncthreads();
+  return v + below;
 }
 
 // One workgroup: expert totals, exclusive scan -> expert_offsets, then each
@@ -247,7 +251,7 @@ __device__ __forceinline__ int32_t block_scan512(int32_t* tot, int32_t v) {
 __global__ __launch_bounds__(512) void perm_scan_kernel(int32_t* __restrict__ counts, int chunks,
                                                         int E, int32_t* __restrict__ offsets,
                                                         int bm, int32_t* __restrict__ mtile_off) {
-  __shared__ int32_t tot[512];
+  __shared__ int32_t tot[8];
   const int e = threadIdx.x;
   // the chunk column of expert e in batches of 16 independent loads (one
   // dependent load per chunk would make the kernel latency-bound)
@@ -353,21 +357,14 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* ex
 __global__ __launch_bounds__(512) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
                                                           int E, int bm,
                                                           int32_t* __restrict__ mtile_off) {
-  __shared__ int32_t tot[512];
+  __shared__ int32_t wtot[8];
   const int e = threadIdx.x;
   int32_t c = 0;
   if (e < E) c = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-  tot[e] = c;
-  __syncthreads();
-  for (int off = 1; off < 512; off <<= 1) {
-    const int32_t v = e >= off ? tot[e - off] : 0;
-    __syncthreads();
-    tot[e] += v;
-    __syncthreads();
-  }
+  const int32_t incl = block_scan512(wtot, c);
   if (e < E) {
-    mtile_off[e] = tot[e] - c;
-    if (e == E - 1) mtile_off[E] = tot[e];
+    mtile_off[e] = incl - c;
+    if (e == E - 1) mtile_off[E] = incl;
   }
 }
 
@@ -396,7 +393,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
     int32_t* __restrict__ mtile_off) {
   __shared__ int32_t sel[kFusedMaxPairs];
   __shared__ int32_t wcnt[kFusedWaves][512];   // per-wave counts, then per-wave bases
-  __shared__ int32_t tot[512];
+  __shared__ int32_t tot[8];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   for (int p = threadIdx.x; p < P; p += kFusedWaves * 64) sel[p] = topk_idx[p];
@@ -409,24 +406,24 @@ __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
   for (int p = p_lo + lane; p < p_hi; p += 64) atomicAdd(&wcnt[wv][sel[p]], 1);
   __syncthreads();
 
-  // expert totals, exclusive scan, per-wave bases
+  // expert totals, then one exclusive scan of (count << 16 | m-tiles): both
+  // totals stay below 2^16 (P <= 2048, m-tiles <= P / bm + E)
   const int e = threadIdx.x;  // E <= 512 < 1024 threads
   int32_t sum = 0;
   if (e < E)
     for (int w = 0; w < kFusedWaves; ++w) sum += wcnt[w][e];
-  if (e < 512) tot[e] = sum;
-  __syncthreads();
-  for (int off = 1; off < 512; off <<= 1) {
-    int32_t v = 0;
-    if (e < 512 && e >= off) v = tot[e - off];
-    __syncthreads();
-    if (e < 512) tot[e] += v;
-    __syncthreads();
-  }
+  const int32_t c = (e < E) ? (sum + bm - 1) / bm : 0;
+  const int32_t packed = (sum << 16) | c;
+  const int32_t incl = block_scan512(tot, packed);
   if (e < E) {
-    int32_t base = tot[e] - sum;
+    const int32_t excl = incl - packed;
+    int32_t base = excl >> 16;
     offsets[e] = base;
-    if (e == E - 1) offsets[E] = tot[e];
+    mtile_off[e] = excl & 0xFFFF;
+    if (e == E - 1) {
+      offsets[E] = incl >> 16;
+      mtile_off[E] = incl & 0xFFFF;
+    }
     for (int w = 0; w < kFusedWaves; ++w) {
       const int32_t n = wcnt[w][e];
       wcnt[w][e] = base;
@@ -434,21 +431,6 @@ __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
     }
   }
   __syncthreads();
-  // m-tile prefix (reuses tot[]): ceil(count / bm) per expert
-  const int32_t c = (e < E) ? (sum + bm - 1) / bm : 0;
-  if (e < 512) tot[e] = c;
-  __syncthreads();
-  for (int off = 1; off < 512; off <<= 1) {
-    int32_t v = 0;
-    if (e < 512 && e >= off) v = tot[e - off];
-    __syncthreads();
-    if (e < 512) tot[e] += v;
-    __syncthreads();
-  }
-  if (e < E) {
-    mtile_off[e] = tot[e] - c;
-    if (e == E - 1) mtile_off[E] = tot[e];
-  }
 
   // stable scatter, each wave over its chunk in order
   for (int r0 = p_lo; r0 < p_hi; r0 += 64) {
