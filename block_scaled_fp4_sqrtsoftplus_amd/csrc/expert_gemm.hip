@@ -151,6 +151,48 @@ __device__ __forceinline__ bool map_tile_grouped(const ExpertGemmArgs& p, int n_
   return true;
 }
 
+// The MT MFMAs of one weight tile in a K step of the generic kernel (FP4
+// weights: A = 16 bytes, cbsz 4; FP8 weights: A = 32 bytes, cbsz 0), from one
+// asm statement; the last of a step (the _g variants) closes it with 32 wait
+// states and takes every scale register of the step (k0..k3: the weight
+// tiles') as an input, so that none is reused before them.  (Plain device
+// functions: templates called from the kernel's lambdas fail overload
+// resolution in the host compilation pass.)
+#define GEN_MFMA(M, CB)                                                                         \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[c" #M "], %[a], %[b" #M "], %[c" #M "], %[sa], %[s" #M \
+  "] op_sel_hi:[0,0,0]" CB "\n\t"
+#define GEN_GUARD "s_nop 15\n\ts_nop 15"
+#define GEN_KA [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3])
+#define GEN_DEF1(NAME, AT, CB, G)                                                              \
+  __device__ __forceinline__ void NAME(v4f* acc, const AT& av, const v8i* bv, uint32_t sa,    \
+                                       const uint32_t* sb, const uint32_t* ka) {              \
+    asm volatile("s_nop 1\n\t" GEN_MFMA(0, CB) G                                             \
+                 : [c0] "+v"(acc[0])                                                          \
+                 : [a] "v"(av), [b0] "v"(bv[0]), [sa] "v"(sa), [s0] "v"(sb[0]), GEN_KA);      \
+  }
+#define GEN_DEF4(NAME, AT, CB, G)                                                              \
+  __device__ __forceinline__ void NAME(v4f* acc, const AT& av, const v8i* bv, uint32_t sa,    \
+                                       const uint32_t* sb, const uint32_t* ka) {              \
+    asm volatile("s_nop 1\n\t" GEN_MFMA(0, CB) GEN_MFMA(1, CB) GEN_MFMA(2, CB) GEN_MFMA(3, CB) G \
+                 : [c0] "+v"(acc[0]), [c1] "+v"(acc[1]), [c2] "+v"(acc[2]), [c3] "+v"(acc[3])  \
+                 : [a] "v"(av), [b0] "v"(bv[0]), [b1] "v"(bv[1]), [b2] "v"(bv[2]),             \
+                   [b3] "v"(bv[3]), [sa] "v"(sa), [s0] "v"(sb[0]), [s1] "v"(sb[1]),            \
+                   [s2] "v"(sb[2]), [s3] "v"(sb[3]), GEN_KA);                                 \
+  }
+GEN_DEF1(gen_fp4_1, v4i, " cbsz:4", "")
+GEN_DEF1(gen_fp4_1_g, v4i, " cbsz:4", GEN_GUARD)
+GEN_DEF1(gen_fp8_1, v8i, "", "")
+GEN_DEF1(gen_fp8_1_g, v8i, "", GEN_GUARD)
+GEN_DEF4(gen_fp4_4, v4i, " cbsz:4", "")
+GEN_DEF4(gen_fp4_4_g, v4i, " cbsz:4", GEN_GUARD)
+GEN_DEF4(gen_fp8_4, v8i, "", "")
+GEN_DEF4(gen_fp8_4_g, v8i, "", GEN_GUARD)
+#undef GEN_DEF1
+#undef GEN_DEF4
+#undef GEN_MFMA
+#undef GEN_GUARD
+#undef GEN_KA
+
 template <int MODE, int MT, bool FP8W = false>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {
@@ -282,16 +324,28 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
       }
     }
     if (wave_live) {
+      // one asm statement per weight tile, one 32-wait-state guard per step
+      // (the last statement, which holds every scale register of the step)
+      typedef typename std::conditional<FP8W, v8i, v4i>::type AV;
+      v8i bv[MT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int m = 0; m < MT; ++m)
+        bv[m] = v8i{(int)x.b[m][0].x, (int)x.b[m][0].y, (int)x.b[m][0].z, (int)x.b[m][0].w,
+                    (int)x.b[m][1].x, (int)x.b[m][1].y, (int)x.b[m][1].z, (int)x.b[m][1].w};
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-          if constexpr (FP8W)
-            acc[t][m] = mfma_fp8_fp8(x.a[t][0], x.a[t][FP8W ? 1 : 0], x.b[m][0], x.b[m][1],
-                                     acc[t][m], (int)x.sa[t], (int)x.sb[m]);
-          else
-            acc[t][m] = mfma_fp4_fp8(x.a[t][0], x.b[m][0], x.b[m][1], acc[t][m], (int)x.sa[t],
-                                     (int)x.sb[m]);
+      for (int t = 0; t < 4; ++t) {
+        AV av;
+        if constexpr (FP8W)
+          av = AV{(int)x.a[t][0].x, (int)x.a[t][0].y, (int)x.a[t][0].z, (int)x.a[t][0].w,
+                  (int)x.a[t][FP8W ? 1 : 0].x, (int)x.a[t][FP8W ? 1 : 0].y,
+                  (int)x.a[t][FP8W ? 1 : 0].z, (int)x.a[t][FP8W ? 1 : 0].w};
+        else
+          av = AV{(int)x.a[t][0].x, (int)x.a[t][0].y, (int)x.a[t][0].z, (int)x.a[t][0].w};
+        if constexpr (FP8W && MT == 1) (t == 3 ? gen_fp8_1_g : gen_fp8_1)(acc[t], av, bv, x.sa[t], x.sb, x.sa);
+        else if constexpr (FP8W) (t == 3 ? gen_fp8_4_g : gen_fp8_4)(acc[t], av, bv, x.sa[t], x.sb, x.sa);
+        else if constexpr (MT == 1) (t == 3 ? gen_fp4_1_g : gen_fp4_1)(acc[t], av, bv, x.sa[t], x.sb, x.sa);
+        else (t == 3 ? gen_fp4_4_g : gen_fp4_4)(acc[t], av, bv, x.sa[t], x.sb, x.sa);
+      }
     }
   };
   // one K step: compute from x (its activations in LDS buffer `buf` when
