@@ -786,18 +786,20 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream8(ExpertGemmAr
 
 // ---------------------------------------------------------------------------
 // Tile variant for m-tiles of 128 pairs (prefill) when K is 1024, 2048 or
-// 4096.  Each of the four waves owns 4 weight tiles (64 rows) streamed into
-// registers through a four-step ring.  The 128 activation rows of a K step
-// are loaded two steps ahead into registers, written to one of four LDS
-// buffers at the end of the step before their use, and read by all four
-// waves.  The 128 tokens' per-128 activation scales and the 256 weight rows'
-// per-32 scale lines sit in LDS for the whole tile.  Per K step a wave
-// issues 32 MFMAs in four asm blocks of 8 (two 16-token sub-tiles x four
-// weight tiles); each block also reads the next block's activations from
-// LDS and waits for them.  The step's scale operands are computed before its
-// first block and held until its last block, which closes with the wait
-// states that protect them and the accumulators (one guard per step instead
-// of one per block).  Accumulators live in AGPRs.
+// 4096: a tile is 128 pairs x 256 weight rows; each of the four waves owns 4
+// weight tiles (64 rows) streamed into registers through a four-step ring.
+// The 128 activation rows of a K step are loaded three steps ahead into
+// registers, written to one of four LDS buffers two steps before their use,
+// and read by all four waves.  The 128 tokens' per-128 activation scales and
+// the 256 weight rows' per-32 scale lines sit in LDS (double-buffered across
+// tiles).  Per K step a wave issues 32 MFMAs in four asm blocks of 8 (two
+// 16-token sub-tiles x four weight tiles); each block also reads the next
+// block's activations from LDS, and the last one the next step's first
+// operands, the next group's scales (every fourth step) and writes the
+// staged activations, all in the shadow of its MFMAs.  Scale operands are
+// held from the step's first block to its last, which closes with the wait
+// states that protect them and the accumulators (one guard per step).
+// Accumulators live in AGPRs.  The grid is persistent (expert_gemm_tile).
 //
 // LDS activation layout: token t's 16-byte chunk c (bytes 16c..16c+15 of the
 // step) sits at slot c ^ (t & 7) of the token's 128-byte line.  With that
