@@ -209,9 +209,8 @@ int choose_bm(const moe_config& c) {
   if (P <= (int64_t)32 * c.n_experts) return 16;
   if (c.expert_format == MOE_EXPERTS_NVFP4 || c.expert_format == MOE_EXPERTS_W4AFP8)
     return (c.hidden <= 4096 && c.inter <= 4096) ? 64 : 16;   // 64-pair tiles need K <= 4096
-  if (c.expert_format == MOE_EXPERTS_FP8) return 64;     // no 128-pair FP8 tile kernel
   auto tiled = [](int k) { return k == 1024 || k == 2048 || k == 4096; };
-  return (tiled(c.hidden) && tiled(c.inter)) ? 128 : 64;
+  return (tiled(c.hidden) && tiled(c.inter)) ? 128 : 64;   // MXFP4 and FP8 tile kernels
 }
 
 // Routing (S1-S3).  Small batches run the single-workgroup permutation

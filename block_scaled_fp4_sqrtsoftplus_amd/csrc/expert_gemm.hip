@@ -820,22 +820,31 @@ constexpr int kTileBuf = 128 * 128;   // bytes of one activation buffer
 // see the transposed scale-line layout in the kernel).  The MFMA takes byte
 // Q of both: op_sel (low bit) and op_sel_hi (high bit) select the byte of
 // each scale operand (measured on gfx950).
+// (FP4 weights: A operand format cbsz 4; FP8 weights: cbsz 0)
 #define TILE_OPSEL_0 "op_sel:[0,0,0] op_sel_hi:[0,0,0]"
 #define TILE_OPSEL_1 "op_sel:[1,1,0] op_sel_hi:[0,0,0]"
 #define TILE_OPSEL_2 "op_sel:[0,0,0] op_sel_hi:[1,1,0]"
 #define TILE_OPSEL_3 "op_sel:[1,1,0] op_sel_hi:[1,1,0]"
 #define TILE_MFMA(C, A, B, S, T, OPS)                                                         \
   "v_mfma_scale_f32_16x16x128_f8f6f4 %[" C "], %[" A "], %[" B "], %[" C "], %[" S "], %[" T \
-  "] " OPS " cbsz:4\n\t"
+  "] " OPS "\n\t"
 #define TILE_MFMA4(C0, C1, C2, C3, B, T, OPS)                                                 \
   TILE_MFMA(C0, "a0", B, "s0", T, OPS) TILE_MFMA(C1, "a1", B, "s1", T, OPS)                   \
   TILE_MFMA(C2, "a2", B, "s2", T, OPS) TILE_MFMA(C3, "a3", B, "s3", T, OPS)
-// the asm statement BODY(op_sel of step Q) with outputs OUTS, inputs INS
-#define TILE_Q_ASM(BODY, OUTS, INS)                                 \
-  if constexpr (Q == 0) asm volatile(BODY(TILE_OPSEL_0) : OUTS : INS); \
-  else if constexpr (Q == 1) asm volatile(BODY(TILE_OPSEL_1) : OUTS : INS); \
-  else if constexpr (Q == 2) asm volatile(BODY(TILE_OPSEL_2) : OUTS : INS); \
-  else asm volatile(BODY(TILE_OPSEL_3) : OUTS : INS)
+// the asm statement BODY(op_sel of step Q, weight format) with outputs
+// OUTS, inputs INS
+#define TILE_Q_ASM(BODY, OUTS, INS)                                                       \
+  if constexpr (F8) {                                                                     \
+    if constexpr (Q == 0) asm volatile(BODY(TILE_OPSEL_0) : OUTS : INS);                  \
+    else if constexpr (Q == 1) asm volatile(BODY(TILE_OPSEL_1) : OUTS : INS);             \
+    else if constexpr (Q == 2) asm volatile(BODY(TILE_OPSEL_2) : OUTS : INS);             \
+    else asm volatile(BODY(TILE_OPSEL_3) : OUTS : INS);                                   \
+  } else {                                                                                \
+    if constexpr (Q == 0) asm volatile(BODY(TILE_OPSEL_0 " cbsz:4") : OUTS : INS);        \
+    else if constexpr (Q == 1) asm volatile(BODY(TILE_OPSEL_1 " cbsz:4") : OUTS : INS);   \
+    else if constexpr (Q == 2) asm volatile(BODY(TILE_OPSEL_2 " cbsz:4") : OUTS : INS);   \
+    else asm volatile(BODY(TILE_OPSEL_3 " cbsz:4") : OUTS : INS);                         \
+  }
 
 #define TILE_ACC_OUT                                                                        \
   [c0] "+a"(c0[0]), [c1] "+a"(c0[1]), [c2] "+a"(c0[2]), [c3] "+a"(c0[3]), [d0] "+a"(c1[0]), \
@@ -876,8 +885,9 @@ __device__ __forceinline__ void tile_read2(v8i& b0, v8i& b1, uint32_t lo, uint32
   TILE_MFMA4("c0", "c1", "c2", "c3", "b0", "t0", OPS)                               \
   TILE_MFMA4("d0", "d1", "d2", "d3", "b1", "t1", OPS) "s_waitcnt lgkmcnt(0)"
 #define TILE_READ_IN TILE_OPND_IN, [t0] "v"(sb0), [t1] "v"(sb1), [o0] "n"(OFF), [o1] "n"(OFF + 2048)
-template <int OFF, int Q>
-__device__ __forceinline__ void tile_mfma8_read(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+template <int OFF, int Q, bool F8 = false>
+__device__ __forceinline__ void tile_mfma8_read(v4f (&c0)[4], v4f (&c1)[4],
+                                                const typename std::conditional<F8, v8i, v4i>::type (&a)[4],
                                                 const v8i& b0, const v8i& b1, const int (&sa)[4],
                                                 int sb0, int sb1, v8i& n0, v8i& n1, uint32_t lo,
                                                 uint32_t hi) {
@@ -966,8 +976,9 @@ __device__ __forceinline__ void tile_read_scales(uint32_t (&tw)[8], uint32_t (&w
   TILE_LAST_IN, [tok] "v"(tok), [wrow] "v"(wrow), [q1] "n"(TROW), [q2] "n"(2 * TROW),      \
       [q3] "n"(3 * TROW), [q4] "n"(4 * TROW), [q5] "n"(5 * TROW), [q6] "n"(6 * TROW),      \
       [q7] "n"(7 * TROW), [p1] "n"(WROW), [p2] "n"(2 * WROW), [p3] "n"(3 * WROW)
-template <int OFFN, int WOFF, bool SC, int TROW, int WROW, int Q>
-__device__ __forceinline__ void tile_mfma8_last_pf(v4f (&c0)[4], v4f (&c1)[4], const v4i (&a)[4],
+template <int OFFN, int WOFF, bool SC, int TROW, int WROW, int Q, bool F8 = false>
+__device__ __forceinline__ void tile_mfma8_last_pf(v4f (&c0)[4], v4f (&c1)[4],
+                                                   const typename std::conditional<F8, v8i, v4i>::type (&a)[4],
                                                    const v8i& b0, const v8i& b1,
                                                    const int (&sa)[4], const int (&sb)[8],
                                                    v8i& n0, v8i& n1, uint32_t lo, uint32_t hi,
@@ -1059,13 +1070,20 @@ __device__ __forceinline__ TileSel decode_tile(const int* mt, const int* eo, int
 // the weight ring, the activation staging and the scale lines of the next
 // tile are loaded while the current tile finishes, so that its epilogue and
 // the next tile's first loads overlap instead of following each other.
-template <int MODE, int S>
+// F8: FP8 weights ([N, K] E4M3 bytes, one scale per row and K step) instead
+// of MXFP4; their 32-byte A operands run through a two-step ring, so that
+// the registers stay those of the four-step ring of 16-byte FP4 operands.
+template <int MODE, int S, bool F8 = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmArgs p,
                                                                      int n_tiles) {
   constexpr int MT = 8, BM = 128;
   constexpr int K = S * 128;
   static_assert(S % 4 == 0 && S >= 8, "K steps in groups of four, at least two groups");
-  constexpr int WLINE = 4 * S + 16;     // weight scale line, padded (banks)
+  constexpr int RD = F8 ? 2 : 4;                // weight ring depth (steps)
+  constexpr int WROWB = F8 ? K : K / 2;         // weight bytes per row
+  constexpr int SROWB = F8 ? S : K / 32;        // weight scale bytes per row
+  constexpr int WLINE = F8 ? S + 16 : 4 * S + 16;  // weight scale line in LDS, padded (banks)
+  typedef typename std::conditional<F8, v8i, v4i>::type AT;
   constexpr int NROWS = MODE == 1 ? kG1Cols : kG2Rows;
   __shared__ __attribute__((aligned(1024))) uint8_t act[4 * kTileBuf];
   __shared__ __attribute__((aligned(16))) uint8_t bsc[2][BM][S];
@@ -1121,12 +1139,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         row0 = live ? ts.n0 + 64 * wv + 16 * t : 16 * t;
       }
       const size_t rr = (size_t)ts.e * N + row0;
-      wb[t] = wbase + rr * (K / 2);
-      sb[t] = sbase + rr * (K / 32);
+      wb[t] = wbase + rr * WROWB;
+      sb[t] = sbase + rr * SROWB;
     }
     return live;
   };
-  const uint32_t wlo = (uint32_t)(col * (K / 2) + 16 * grp);
+  const uint32_t wlo = (uint32_t)(col * WROWB + 16 * grp);
 
   // activation staging: this thread moves 4 x 16 bytes per step, for tile
   // tokens 32*wv + 8*j + lane/8 (j = 0..3), landing at slot lane%8 of the
@@ -1147,10 +1165,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<v4i*>(act + q * kTileBuf + sdst + 1024 * j) = rg[j];
   };
-  v4i A[4][4];  // weight ring: [step % 4][tile]
-  auto load_a = [&](const uint8_t* const (&wb)[4], int s, v4i (&a)[4]) {
+  AT A[RD][4];  // weight ring: [step % RD][tile]
+  auto load_a = [&](const uint8_t* const (&wb)[4], int s, AT (&a)[4]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = gload<v4i>(wb[t] + wlo + s * 64);
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (F8) {
+        // the two 64-byte halves of the row's step line back to back
+        const v4i lo = gload<v4i>(wb[t] + wlo + s * 128);
+        const v4i hi = gload<v4i>(wb[t] + wlo + s * 128 + 64);
+        a[t] = AT{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        a[t] = gload<v4i>(wb[t] + wlo + s * 64);
+      }
+    }
   };
 
   // Weight scale lines in LDS, transposed per group of four K steps: the
@@ -1175,6 +1202,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 #pragma unroll
     for (int k = 0; k < CPS; ++k) w.c[k] = i0 + k < NG ? gload<v4i>(wgroup_src(sbp, i0 + k)) : v4i{0, 0, 0, 0};
     return w;
+  };
+  // FP8: one scale byte per row and step, no transpose (the four lane groups
+  // read the same dword); lane (grp, col) copies row 16*grp + col's line
+  typedef typename std::conditional<S == 8, v2i, v4i>::type F8Chunk;
+  constexpr int F8N = S == 8 ? 1 : S / 16;
+  struct F8Line { F8Chunk c[F8N]; };
+  auto f8line_load = [&](const uint8_t* const (&sbp)[4]) {
+    F8Line w;
+    const uint8_t* src = sel4(sbp, grp) + col * S;
+#pragma unroll
+    for (int k = 0; k < F8N; ++k) w.c[k] = gload<F8Chunk>(src + k * sizeof(F8Chunk));
+    return w;
+  };
+  auto f8line_store = [&](int b, const F8Line& w) {
+#pragma unroll
+    for (int k = 0; k < F8N; ++k)
+      reinterpret_cast<F8Chunk*>(&wsc[b][wv][16 * grp + col][0])[k] = w.c[k];
   };
   // 4x4 byte transpose of a 16-byte group (dword q, byte kb -> dword kb, byte q)
   auto transpose16 = [](const v4i& d) {
@@ -1222,8 +1266,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
 #pragma unroll
     for (int j = 0; j < 4; ++j) ssrc[j] = p.a + (size_t)rows[j] * K + 16 * a_slot;
     tline_store(0, gload<TChunk>(tline_src(srow)));
+    if constexpr (F8) {
+      f8line_store(0, f8line_load(sb));
+    } else {
 #pragma unroll
-    for (int i0 = 0; i0 < NG; i0 += CPS) wline_store(0, i0, wline_load(sb, i0));
+      for (int i0 = 0; i0 < NG; i0 += CPS) wline_store(0, i0, wline_load(sb, i0));
+    }
   }
 
   v4f acc[MT][4];
@@ -1241,8 +1289,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   stage_load(ssrc, 0, R2[0]);
   load_a(wb, 1, A[1]);
   stage_load(ssrc, 1, R2[1]);
-  load_a(wb, 2, A[2]);
-  load_a(wb, 3, A[3]);
+  if constexpr (RD == 4) {
+    load_a(wb, 2, A[2 % RD]);
+    load_a(wb, 3, A[3 % RD]);
+  }
   stage_store(0, R2[0]);
   stage_store(1, R2[1]);
   stage_load(ssrc, 2, R2[0]);
@@ -1256,7 +1306,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   v8i x0, x1;
   lds_barrier();
   tile_read_scales<16 * S, 16 * WLINE>(sbw, saw, lds_addr(&bsc[0][col][0]),
-                                       lds_addr(&wsc[0][wv][col][4 * grp]));
+                                       lds_addr(&wsc[0][wv][col][F8 ? 0 : 4 * grp]));
   tile_read2<0>(x0, x1, rd_lo, rd_hi);
 
   using I0 = std::integral_constant<int, 0>;
@@ -1267,10 +1317,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
   for (int jt = 0; jt < n_my; ++jt) {
     const int cb = jt & 1, nb = cb ^ 1;  // scale buffers of this and the next tile
     const uint32_t sc_tok = lds_addr(&bsc[cb][col][0]);
-    const uint32_t sc_w = lds_addr(&wsc[cb][wv][col][4 * grp]);
+    const uint32_t sc_w = lds_addr(&wsc[cb][wv][col][F8 ? 0 : 4 * grp]);
 
     const uint32_t nsc_tok = lds_addr(&bsc[nb][col][0]);
-    const uint32_t nsc_w = lds_addr(&wsc[nb][wv][col][4 * grp]);
+    const uint32_t nsc_w = lds_addr(&wsc[nb][wv][col][F8 ? 0 : 4 * grp]);
 
     // One K step from buffer Q (compile-time) and ring slot Q; its operands
     // for sub-tiles 0, 1 (x0, x1) and, at Q == 0, the group's scales were
@@ -1294,15 +1344,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
       v8i y0, y1;
       // one guard per step: every scale register of the step stays live
       // until the last block, which closes with the wait states
-      tile_mfma8_read<B + 2 * 2048, Q>(acc[0], acc[1], A[Q], x0, x1, sa, sbv[0], sbv[1], y0, y1,
+      tile_mfma8_read<B + 2 * 2048, Q, F8>(acc[0], acc[1], A[Q % RD], x0, x1, sa, sbv[0], sbv[1], y0, y1,
                                     rd_lo, rd_hi);
-      tile_mfma8_read<B + 4 * 2048, Q>(acc[2], acc[3], A[Q], y0, y1, sa, sbv[2], sbv[3], x0, x1,
+      tile_mfma8_read<B + 4 * 2048, Q, F8>(acc[2], acc[3], A[Q % RD], y0, y1, sa, sbv[2], sbv[3], x0, x1,
                                     rd_lo, rd_hi);
-      tile_mfma8_read<B + 6 * 2048, Q>(acc[4], acc[5], A[Q], x0, x1, sa, sbv[4], sbv[5], y0, y1,
+      tile_mfma8_read<B + 6 * 2048, Q, F8>(acc[4], acc[5], A[Q % RD], x0, x1, sa, sbv[4], sbv[5], y0, y1,
                                     rd_lo, rd_hi);
       const uint32_t tok = LAST ? nsc_tok : sc_tok + s + 1;
-      const uint32_t wrow = LAST ? nsc_w : sc_w + 4 * (s + 1);
-      tile_mfma8_last_pf<BN, WB, Q == 3, 16 * S, 16 * WLINE, Q>(acc[6], acc[7], A[Q], y0, y1, sa,
+      const uint32_t wrow = LAST ? nsc_w : sc_w + (F8 ? 1 : 4) * (s + 1);
+      tile_mfma8_last_pf<BN, WB, Q == 3, 16 * S, 16 * WLINE, Q, F8>(acc[6], acc[7], A[Q % RD], y0, y1, sa,
                                                              sbv, x0, x1, rd_lo, rd_hi,
                                                              R2[Q & 1], st_wa, sbw, saw, tok,
                                                              wrow);
@@ -1319,6 +1369,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     const uint8_t* nss[4];
     int nraw[4], nraw_s;
     WLine wtmp[2];  // loaded at P into [(P-1)&1], stored at P+1
+    F8Line ftmp;    // FP8: loaded at P1, stored at P2
     TChunk ttmp;
     auto prep_load = [&](auto pc) {
       constexpr int P = decltype(pc)::value;
@@ -1333,7 +1384,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
         const int ps = pair_slot(nxt, tid >> 1);
         nraw_s = MODE == 1 ? gload<int>(p.sorted_pairs + ps) : ps;
       } else if constexpr (P >= 1 && P <= 4) {
-        wtmp[(P - 1) & 1] = wline_load(nsb, (P - 1) * CPS);
+        if constexpr (F8) {
+          if constexpr (P == 1) ftmp = f8line_load(nsb);
+        } else {
+          wtmp[(P - 1) & 1] = wline_load(nsb, (P - 1) * CPS);
+        }
         if constexpr (P == 4) {
           ttmp = gload<TChunk>(tline_src(MODE == 1 ? nraw_s / p.top_k : nraw_s));
 #pragma unroll
@@ -1344,14 +1399,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     };
     auto prep_store = [&](auto pc) {
       constexpr int P = decltype(pc)::value;
-      if constexpr (P >= 2 && P <= 5) wline_store(nb, (P - 2) * CPS, wtmp[P & 1]);
+      if constexpr (F8) {
+        if constexpr (P == 2) f8line_store(nb, ftmp);
+      } else if constexpr (P >= 2 && P <= 5) {
+        wline_store(nb, (P - 2) * CPS, wtmp[P & 1]);
+      }
       if constexpr (P == 5) tline_store(nb, ttmp);
     };
 
     // Step s: barrier; activation loads for step s+3 into registers;
-    // compute(s) from buffer s%4 and ring slot s%4, writing step s+2's
+    // compute(s) from buffer s%4 and ring slot s%RD, writing step s+2's
     // activations (loaded during step s-1) to buffer (s+2)%4 (last read in
-    // step s-2, before the barrier of step s-1); weight loads for step s+4
+    // step s-2, before the barrier of step s-1); weight loads for step s+RD
     // into the ring slot.  Steps past the tile's last come from the next
     // tile.  PREP: compile-time index of the next tile's preparation work;
     // MID: a step of the middle loop (s + 4 < S).
@@ -1363,8 +1422,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_tile(ExpertGemmAr
     else stage_load(nss, (s) + 3 - S, R2[(q_ + 1) & 1]);                         \
     prep_load(std::integral_constant<int, PREP>{});                              \
     compute((s), QC{}, std::integral_constant<bool, !(MID) && (s) == S - 1>{});  \
-    if ((MID) || (s) + 4 < S) load_a(wb, (s) + 4, A[q_]);                        \
-    else load_a(nwb, (s) + 4 - S, A[q_]);                                        \
+    if ((MID) || (s) + RD < S) load_a(wb, (s) + RD, A[q_ % RD]);                 \
+    else load_a(nwb, (s) + RD - S, A[q_ % RD]);                                  \
     prep_store(std::integral_constant<int, PREP>{});                             \
   } while (0)
     TILE_STEP(0, I0, 0, 0);
@@ -1514,6 +1573,21 @@ static hipError_t launch_mode(const ExpertGemmArgs& a, int bm, int mt_max, hipSt
   const int n_tiles = MODE == 1 ? a.N / kG1Cols : (a.N + kG2Rows - 1) / kG2Rows;
   const unsigned grid = pad8((int64_t)n_tiles * mt_max);
   if (grid == 0) return hipSuccess;
+  if (a.fp8w && bm == 128) {
+    if (a.K != 1024 && a.K != 2048 && a.K != 4096) return hipErrorInvalidValue;
+    if (a.E > kMaxExperts) return hipErrorInvalidValue;
+    const unsigned pgrid = std::min(grid, (unsigned)persistent_workgroups());
+    if (a.K == 4096)
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 32, true>), dim3(pgrid), dim3(kGemmThreads), 0, st,
+                         a, n_tiles);
+    else if (a.K == 2048)
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 16, true>), dim3(pgrid), dim3(kGemmThreads), 0, st,
+                         a, n_tiles);
+    else
+      hipLaunchKernelGGL((expert_gemm_tile<MODE, 8, true>), dim3(pgrid), dim3(kGemmThreads), 0, st,
+                         a, n_tiles);
+    return hipGetLastError();
+  }
   if (a.fp8w) {
     if (bm == 16 && a.K == 4096)
       hipLaunchKernelGGL((expert_gemm_stream8<MODE, 32>), dim3(grid), dim3(kGemmThreads), 0, st, a,

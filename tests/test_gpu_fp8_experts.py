@@ -52,8 +52,10 @@ def test_cast_bit_exact(spread):
     ("decode", 8, dict(n_experts=16)),                                 # streaming, K = 4096 / 2048
     ("decode", 10, dict(hidden=1024, inter=1024, n_experts=8)),        # streaming, K = 1024
     ("tiny", 37, dict(hidden=512, inter=384, n_experts=12, top_k=3)),  # 16-pair tiles, other K
-    ("tiny", 200, dict(hidden=256, inter=256, n_experts=8, top_k=2)),  # 64-pair tiles
-    ("decode", 400, dict(n_experts=8, top_k=2)),                       # 64-pair tiles, full K
+    ("decode", 400, dict(n_experts=8, top_k=2)),                       # 128-pair tiles, full K
+    ("decode", 600, dict(hidden=1024, inter=1024, n_experts=8, top_k=2)),  # 128-pair tiles, K = 1024
+    ("decode", 300, dict(hidden=2048, inter=4096, n_experts=4, top_k=2)),  # K = 2048 / 4096 swapped
+    ("tiny", 200, dict(hidden=256, inter=256, n_experts=8, top_k=2)),  # (64-pair tiles: K = 256)
 ])
 def test_fp8_expert_ffn_parity(shape):
     name, tokens, over = shape
