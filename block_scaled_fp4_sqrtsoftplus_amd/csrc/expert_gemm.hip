@@ -44,7 +44,9 @@
 // prefix over experts (mtile_off), so expert counts never travel to the host.
 // Workgroup ids are remapped so that the tiles of one weight n-tile that land
 // on the same XCD (ids are dealt round-robin over the 8 XCDs) are processed
-// together there, and share that XCD's L2.
+// together there, and share that XCD's L2.  The 128-pair tile kernel
+// (prefill) is persistent instead: one workgroup per CU walks a share of the
+// tiles in the same XCD-local, expert-major order.
 #include "moe_internal.h"
 
 #include <algorithm>
@@ -116,36 +118,6 @@ __device__ __forceinline__ bool map_tile(const ExpertGemmArgs& p, int mt_max, in
   }
   e = lo;
   m0 = (mt - p.mtile_off[e]) * bm;
-  off_e = p.expert_offsets[e];
-  n_e = p.expert_offsets[e + 1] - off_e;
-  return true;
-}
-
-// Expert-major tile order for large m-tiles: the tiles of one expert are
-// consecutive, m-tile fastest (an n-slice of its weights is used by all of
-// its m-tiles back to back, and its activation rows by all n-slices close in
-// time), and each XCD (workgroups are dispatched to the 8 XCDs round-robin)
-// takes one contiguous eighth of the real tiles, so that the workgroups
-// sharing an L2 share weights and activations.
-__device__ __forceinline__ bool map_tile_grouped(const ExpertGemmArgs& p, int n_tiles, int bm,
-                                                 int& n_tile, int& e, int& m0, int& off_e,
-                                                 int& n_e) {
-  const int b = blockIdx.x;
-  const int total = p.mtile_off[p.E] * n_tiles;
-  const int share = (total + 7) >> 3;
-  const int r = b >> 3;
-  const int u = (b & 7) * share + r;
-  if (r >= share || u >= total) return false;
-  int lo = 0, hi = p.E;  // mtile_off[lo] * n_tiles <= u < mtile_off[hi] * n_tiles
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.mtile_off[mid] * n_tiles <= u) lo = mid; else hi = mid;
-  }
-  e = lo;
-  const int m_e = p.mtile_off[e + 1] - p.mtile_off[e];
-  const int local = u - p.mtile_off[e] * n_tiles;
-  n_tile = local / m_e;
-  m0 = (local - n_tile * m_e) * bm;
   off_e = p.expert_offsets[e];
   n_e = p.expert_offsets[e + 1] - off_e;
   return true;
@@ -1038,7 +1010,12 @@ struct TileSel {
   int e, n0, m0, off_e, n_e;
 };
 
-// Tile u of the expert-major order (m-tile fastest; see map_tile_grouped)
+// Expert-major tile order: the tiles of one expert are consecutive, m-tile
+// fastest (an n-slice of its weights is used by all of its m-tiles back to
+// back, and its activation rows by all n-slices close in time); each XCD
+// (workgroups are dealt to the 8 XCDs round-robin) takes one contiguous
+// eighth of the tiles, so that the workgroups sharing an L2 share weights
+// and activations.  Tile u of that order is decoded here
 // from LDS copies of the m-tile prefix (mt) and the expert offsets (eo):
 // e is the number of entries mt[i] * n_tiles <= u, minus one, counted by the
 // whole wave at once.  Wave-uniform.
