@@ -105,12 +105,18 @@ def test_layer_token_permutation_equivariant():
     assert np.array_equal(y2, y[perm])
 
 
-SAMPLE = {"decode": 16, "prefill": 12, "skewed": 8, "hash": 8}
+SAMPLE = {"decode": 16, "prefill": 12, "skewed": 8, "hash": 8, "e512": 8}
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "hash"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "hash", "e512"])
 def test_layer_full_size_sampled(name):
-    wl = synth.WORKLOADS[name]
+    if name == "e512":
+        # the largest expert count through the 128-pair tile kernel: 20480
+        # pairs over 512 experts (40 per expert), K = 1024
+        wl = synth.WORKLOADS["decode"].replace(name="e512", tokens=2560, hidden=1024, inter=1024,
+                                               n_experts=512, top_k=8)
+    else:
+        wl = synth.WORKLOADS[name]
     print(f"[{name}] generating inputs T={wl.tokens} E={wl.n_experts}", flush=True)
     inp = synth.make_inputs(wl)
     d = device_inputs(inp)
