@@ -104,6 +104,7 @@ struct LayerWs {
   float* o;
   uint16_t* hsh;
   float* ysh;
+  float* shpart;
 };
 LayerWs carve_layer(Carver& cv, const moe_config& c) {
   const int64_t P = c.tokens * c.top_k;
@@ -120,6 +121,7 @@ LayerWs carve_layer(Carver& cv, const moe_config& c) {
   l.o = cv.take<float>((size_t)P * c.hidden);
   l.hsh = cv.take<uint16_t>((size_t)c.tokens * c.inter);
   l.ysh = cv.take<float>((size_t)c.tokens * c.hidden);
+  l.shpart = cv.take<float>((size_t)shared_part_floats(c.tokens, c.hidden, c.inter));
   return l;
 }
 
@@ -221,33 +223,41 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
                          const float* bias, const int64_t* ids, const float* logits_in,
                          float* logits_out, const moe_routing& r, const RouteWs& ws,
                          hipStream_t st, int32_t* mtile_off = nullptr, bool* tiles_done = nullptr,
-                         uint8_t* xq = nullptr, uint8_t* xs = nullptr) {
+                         uint8_t* xq = nullptr, uint8_t* xs = nullptr,
+                         const SharedFused* sf = nullptr) {
   const int64_t T = c.tokens, P = T * c.top_k;
   if (tiles_done) *tiles_done = false;
+  // the shared expert rides only in the split-K router / fused permutation launches
+  if (sf && !(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && !logits_in &&
+              router_tile_splits(T, c.hidden, c.n_experts) == 1 &&
+              router_splits(T, c.hidden) > 1 && P > 0 && P <= kFusedMaxPairs))
+    return MOE_ERR_UNSUPPORTED;
   if (c.route_mode == MOE_ROUTE_HASH) {
     MOE_TRY(launch_hash_route(ids, T, c.n_experts, c.top_k, c.route_scale, c.hash_seed,
                               r.topk_idx, r.topk_w, st));
   } else if (logits_in) {
     MOE_TRY(launch_score_topk(logits_in, 1, logits_out, bias, T, c.n_experts, c.top_k,
-                              c.route_scale, r.topk_idx, r.topk_w, st));
+                              c.route_scale, r.topk_idx, r.topk_w, nullptr, st));
   } else if (router_tile_splits(T, c.hidden, c.n_experts) > 1) {
     const int ks = router_tile_splits(T, c.hidden, c.n_experts);
     MOE_TRY(launch_router_tile_split(x, wg, ws.logits, T, c.hidden, c.n_experts, ks, st));
     MOE_TRY(launch_score_topk(ws.logits, ks, logits_out, bias, T, c.n_experts, c.top_k,
-                              c.route_scale, r.topk_idx, r.topk_w, st));
+                              c.route_scale, r.topk_idx, r.topk_w, nullptr, st));
   } else if (router_splits(T, c.hidden) > 1) {
-    MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, xq, xs, st));
+    MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, xq, xs, sf, st));
     MOE_TRY(launch_score_topk(ws.logits, router_splits(T, c.hidden), logits_out, bias, T,
-                              c.n_experts, c.top_k, c.route_scale, r.topk_idx, r.topk_w, st));
+                              c.n_experts, c.top_k, c.route_scale, r.topk_idx, r.topk_w, sf,
+                              st));
   } else {
     float* dst = logits_out ? logits_out : ws.logits;
     MOE_TRY(launch_router_gemm(x, wg, dst, T, c.hidden, c.n_experts, st));
     MOE_TRY(launch_score_topk(dst, 1, nullptr, bias, T, c.n_experts, c.top_k, c.route_scale,
-                              r.topk_idx, r.topk_w, st));
+                              r.topk_idx, r.topk_w, nullptr, st));
   }
   if (P > 0 && P <= kFusedMaxPairs) {
     MOE_TRY(launch_perm_fused(r.topk_idx, (int)P, c.n_experts, choose_bm(c), r.expert_offsets,
-                              r.sorted_pairs, r.pair_pos, mtile_off ? mtile_off : ws.mtile_off, st));
+                              r.sorted_pairs, r.pair_pos, mtile_off ? mtile_off : ws.mtile_off,
+                              sf, st));
     if (tiles_done) *tiles_done = mtile_off != nullptr;
     return MOE_OK;
   }
@@ -466,15 +476,31 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   if (c.tokens == 0)
     return enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st);
 
-  // Caller's stream: quantize x, route, routed experts, combine.  The shared
-  // expert (which needs only x) runs on the side stream and joins before the
-  // combine.  Small batches fork it once routing is enqueued, so that it
-  // overlaps the bandwidth-bound expert GEMMs rather than the latency-bound
-  // routing kernels (forking first cost 2% at T = 64); batches of at least
+  // Caller's stream: quantize x, route, routed experts, combine.  Decode-sized
+  // batches with score routing carry the shared expert inside the routing
+  // launches (split-K up projection beside the router, SwiGLU beside the
+  // top-k, split-K down projection beside the permutation; the combine adds
+  // the down slices): one stream, no fork and join, whose two cross-stream
+  // waits cost ~5 us each at T = 64.  Otherwise the shared expert (which
+  // needs only x) runs on the side stream and joins before the combine.
+  // Small batches fork it once routing is enqueued, so that it overlaps the
+  // bandwidth-bound expert GEMMs rather than the latency-bound routing
+  // kernels (forking first cost 2% at T = 64); batches of at least
   // kEarlyForkTokens fork it first, where its GEMMs are long enough to fill
   // the GPU the routing kernels leave idle (1.6% less layer time at
   // T = 32768, the same at T = 4096).
+  const bool quant_in_router =
+      c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && router_splits(c.tokens, c.hidden) > 1;
+  const bool fused_shared = shared && quant_in_router &&
+                            router_tile_splits(c.tokens, c.hidden, c.n_experts) == 1 &&
+                            shared_split_ok(c.tokens, c.hidden, c.inter) &&
+                            c.tokens * c.top_k <= kFusedMaxPairs;
+  SharedFused sf{};
+  if (fused_shared)
+    sf = SharedFused{shared->w1, shared->w3, shared->w2, l.hsh, l.shpart, (int)c.tokens,
+                     c.hidden, c.inter, c.swiglu_limit};
   const float* ysh = nullptr;
+  int ysh_parts = 1;
   std::unique_lock<std::mutex> lock;
   SideStream* side = nullptr;
   auto fork_shared = [&]() -> moe_status {
@@ -484,30 +510,36 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
     hipStream_t ss = side->stream;
     MOE_TRY(hipEventRecord(side->fork, st));
     MOE_TRY(hipStreamWaitEvent(ss, side->fork, 0));
-    MOE_TRY(launch_shared_up(x, shared->w1, shared->w3, l.hsh, c.tokens, c.hidden, c.inter,
-                             c.swiglu_limit, ss));
-    MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, c.tokens, c.hidden, c.inter, ss));
+    MOE_TRY(launch_shared_up(x, shared->w1, shared->w3, l.hsh, l.shpart, c.tokens, c.hidden,
+                             c.inter, c.swiglu_limit, ss));
+    MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, l.shpart, c.tokens, c.hidden, c.inter,
+                               ss));
     MOE_TRY(hipEventRecord(side->join, ss));
     ysh = l.ysh;
     return MOE_OK;
   };
-  const bool early_fork = shared && c.tokens >= kEarlyForkTokens;
+  const bool side_shared = shared && !fused_shared;
+  const bool early_fork = side_shared && c.tokens >= kEarlyForkTokens;
   if (early_fork && (s = fork_shared()) != MOE_OK) return s;
   // small score-routed batches quantize x inside the split-K router launch
-  const bool quant_in_router =
-      c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && router_splits(c.tokens, c.hidden) > 1;
   if (!quant_in_router) MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
   bool tiles_done = false;
   if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
                          l.ffn.mtile_off, &tiles_done, quant_in_router ? l.xq : nullptr,
-                         quant_in_router ? l.xs : nullptr)) != MOE_OK)
+                         quant_in_router ? l.xs : nullptr,
+                         fused_shared ? &sf : nullptr)) != MOE_OK)
     return s;
-  if (shared && !early_fork && (s = fork_shared()) != MOE_OK) return s;
+  if (side_shared && !early_fork && (s = fork_shared()) != MOE_OK) return s;
   if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,
                        tiles_done)) != MOE_OK)
     return s;
-  if (shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
-  MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, y, c.tokens, c.hidden, c.top_k, st));
+  if (side_shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
+  if (fused_shared) {
+    ysh = l.shpart;
+    ysh_parts = c.inter / kSharedSplitK;
+  }
+  MOE_TRY(launch_combine(l.o, r.topk_w, r.pair_pos, ysh, ysh_parts, y, c.tokens, c.hidden,
+                         c.top_k, st));
   return MOE_OK;
 }
 

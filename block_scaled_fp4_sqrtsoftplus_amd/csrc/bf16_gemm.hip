@@ -13,21 +13,13 @@
 //   EPI_SWIGLU tiles 0..TPW/2-1 read w1 rows, the rest w3 rows of the same
 //              columns; out[t][n] = bf16(silu(clip(g)) * clip(u))
 #include "moe_internal.h"
+#include "shared_splitk.h"
 
 #include <type_traits>
 
 namespace moe {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-
-enum { EPI_F32 = 0, EPI_SWIGLU = 1 };
-
-__device__ __forceinline__ v4f mfma_bf16(const uint4& a, const uint4& b, v4f acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
 
 template <int EPI, int TPW, int MT>
 __global__ __launch_bounds__(256) void bf16_gemm_kernel(const uint16_t* __restrict__ X,
@@ -284,6 +276,44 @@ static hipError_t launch_skinny(const uint16_t* X, const uint16_t* W, const uint
 }
 
 // ---------------------------------------------------------------------------
+// Decode-sized shared expert on its own stream (the split-K bodies of
+// shared_splitk.h): the skinny kernel above gives every workgroup all of K
+// for 16 weight rows, so the token rows are re-read from L2 twice (up) or four
+// times (down) per weight byte and only 128 workgroups run the up projection;
+// split-K runs 256 workgroups at H = 4096, I = 2048 (up: 64 h columns x 8
+// slices, down: 64 rows x 4 slices), the token slice read once per workgroup.
+// ---------------------------------------------------------------------------
+template <int EPI, int RW>
+__global__ __launch_bounds__(512) void bf16_splitk_kernel(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ W,
+                                                          const uint16_t* __restrict__ W3,
+                                                          float* __restrict__ P, int M, int N,
+                                                          int K) {
+  __shared__ uint4 xs[64][64];
+  shared_splitk_body<EPI, 8, RW>(X, W, W3, P, M, N, K, blockIdx.x, blockIdx.y, xs);
+}
+
+__global__ __launch_bounds__(256) void splitk_swiglu_kernel(const float* __restrict__ P, int S,
+                                                            int M, int N, float limit,
+                                                            uint16_t* __restrict__ h) {
+  shared_swiglu_body(P, S, M, N, limit, h, blockIdx.x * 256 + threadIdx.x);
+}
+
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ P, int S, int M,
+                                                         int N, float* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * (N / 4)) return;
+  const size_t stride = (size_t)M * N;
+  const float* p = P + 4 * (size_t)i;
+  float4 a = *reinterpret_cast<const float4*>(p);
+  for (int s = 1; s < S; ++s) {
+    const float4 b = *reinterpret_cast<const float4*>(p + s * stride);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  *reinterpret_cast<float4*>(y + 4 * (size_t)i) = a;
+}
+
+// ---------------------------------------------------------------------------
 // Router logits of a small batch (M <= 64 tokens): the gate matrix is only
 // E x H bf16 (2 MB at E = 256), so the whole read must be in flight at once.
 // Workgroup (nb, ks) of 8 waves owns 16 experts and the K slice
@@ -293,27 +323,48 @@ static hipError_t launch_skinny(const uint16_t* X, const uint16_t* W, const uint
 // in ks order, so the logits do not depend on timing.  With q, the same
 // workgroups also quantize x to FP8 (the layer's next step, which reads the
 // same rows): 32 blocks of 128 per workgroup and pass, one launch fewer.
+// Workgroups are numbered ks * ceil(N / 16) + nb; with sh.blocks > 0 the
+// workgroups after the router's run the shared expert's split-K up
+// projection (it reads the same x), which then needs no launch of its own.
 // ---------------------------------------------------------------------------
+// Shared-expert up projection riding in the router launch (blocks = 0: none).
+struct SharedUpArgs {
+  const uint16_t* w1;
+  const uint16_t* w3;
+  float* part;
+  int I;
+  int blocks;
+};
+
 template <int MT, int STEPS>
 __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ W,
                                                             float* __restrict__ partial, int M,
                                                             int N, int K, int KS,
                                                             uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ qscale) {
+                                                            uint8_t* __restrict__ qscale,
+                                                            SharedUpArgs sh) {
   constexpr int NACC = MT * 4;
-  __shared__ float red[4][NACC][64];
+  __shared__ uint4 lds[64][64];   // the router's reduction tree, or the split-K token slice
+  const int gx = (N + 15) / 16;
+  const int rb = blockIdx.x;
+  if (rb >= gx * KS) {
+    const int b = rb - gx * KS, nbx = sh.I / shared_splitk_rows<EPI_SWIGLU, 4>();
+    shared_splitk_body<EPI_SWIGLU, 8, 4>(X, sh.w1, sh.w3, sh.part, M, sh.I, K, b % nbx, b / nbx,
+                                         lds);
+    return;
+  }
+  float (*red)[NACC][64] = reinterpret_cast<float (*)[NACC][64]>(&lds[0][0]);
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int ks = blockIdx.y;
+  const int n0 = (rb % gx) * 16;
+  const int ks = rb / gx;
   if (q) {
     const int64_t n_blocks = (int64_t)M * (K / 128);
-    const int64_t stride = (int64_t)gridDim.x * gridDim.y * 32;
-    for (int64_t b = ((int64_t)ks * gridDim.x + blockIdx.x) * 32 + (threadIdx.x >> 4); b < n_blocks;
-         b += stride)
+    const int64_t stride = (int64_t)gx * KS * 32;
+    for (int64_t b = (int64_t)rb * 32 + (threadIdx.x >> 4); b < n_blocks; b += stride)
       quant_act_block(X, b, n_blocks, threadIdx.x & 15, q, qscale);
   }
   const int k0 = ks * (K / KS) + wv * STEPS * 32;
@@ -594,14 +645,20 @@ int router_splits(int64_t T, int H) {
 }
 
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
-                                 int H, int E, uint8_t* q, uint8_t* scale, hipStream_t st) {
+                                 int H, int E, uint8_t* q, uint8_t* scale, const SharedFused* sf,
+                                 hipStream_t st) {
   const int KS = kRouterSplits;
   const int steps = H / KS / 8 / 32;   // per wave
-  const dim3 grid((unsigned)((E + 15) / 16), (unsigned)KS);
+  SharedUpArgs sh{};
+  if (sf) {
+    sh = SharedUpArgs{sf->w1, sf->w3, sf->part, sf->I,
+                      (sf->I / shared_splitk_rows<EPI_SWIGLU, 4>()) * (H / kSharedSplitK)};
+  }
+  const dim3 grid((unsigned)((E + 15) / 16 * KS + sh.blocks));
   const int M = (int)T;
 #define MOE_ROUTER_LAUNCH(MT, ST) \
   hipLaunchKernelGGL((router_splitk_kernel<MT, ST>), grid, dim3(512), 0, st, x, wg, partial, M, E, H, KS, \
-                     q, scale)
+                     q, scale, sh)
   const int mt = (M + 15) / 16;
   if (steps == 2) {
     if (mt == 1) MOE_ROUTER_LAUNCH(1, 2); else if (mt == 2) MOE_ROUTER_LAUNCH(2, 2);
@@ -617,14 +674,40 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* p
   return hipGetLastError();
 }
 
-hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
-                            uint16_t* h, int64_t T, int H, int I, float limit, hipStream_t st) {
-  return launch_bf16<EPI_SWIGLU, 2>(x, w1, w3, h, T, I, H, limit, st);
+bool shared_split_ok(int64_t T, int H, int I) {
+  return T >= 1 && T <= 64 && H % kSharedSplitK == 0 && I % kSharedSplitK == 0;
 }
 
-hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, int64_t T,
-                              int H, int I, hipStream_t st) {
-  return launch_bf16<EPI_F32, 1>(h, w2, nullptr, ysh, T, H, I, 0.f, st);
+int64_t shared_part_floats(int64_t T, int H, int I) {
+  if (!shared_split_ok(T, H, I)) return 0;
+  const int64_t up = (int64_t)(H / kSharedSplitK) * T * 2 * I;
+  const int64_t down = (int64_t)(I / kSharedSplitK) * T * H;
+  return up > down ? up : down;
+}
+
+hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                            uint16_t* h, float* part, int64_t T, int H, int I, float limit,
+                            hipStream_t st) {
+  if (!part || !shared_split_ok(T, H, I))
+    return launch_bf16<EPI_SWIGLU, 2>(x, w1, w3, h, T, I, H, limit, st);
+  const int S = H / kSharedSplitK, M = (int)T;
+  hipLaunchKernelGGL((bf16_splitk_kernel<EPI_SWIGLU, 4>), dim3((unsigned)(I / 64), (unsigned)S),
+                     dim3(512), 0, st, x, w1, w3, part, M, I, H);
+  hipLaunchKernelGGL(splitk_swiglu_kernel, dim3((unsigned)((M * (I / 4) + 255) / 256)), dim3(256),
+                     0, st, part, S, M, I, limit, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, float* part,
+                              int64_t T, int H, int I, hipStream_t st) {
+  if (!part || !shared_split_ok(T, H, I))
+    return launch_bf16<EPI_F32, 1>(h, w2, nullptr, ysh, T, H, I, 0.f, st);
+  const int S = I / kSharedSplitK, M = (int)T;
+  hipLaunchKernelGGL((bf16_splitk_kernel<EPI_F32, 2>), dim3((unsigned)(H / 64), (unsigned)S),
+                     dim3(512), 0, st, h, w2, nullptr, part, M, H, I);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((M * (H / 4) + 255) / 256)), dim3(256), 0,
+                     st, part, S, M, H, ysh);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -3,7 +3,9 @@
 // routing-weighted sum of its selected experts, plus the shared expert):
 //   y[t] = bf16( sum_j w[t,j] * o[pair_pos[t*k + j]] + ysh[t] )
 // summed in fp32 in rank order j.  A gather (one thread per 4 columns of one
-// token), so the result is deterministic: no atomics.
+// token), so the result is deterministic: no atomics.  The shared expert's
+// output may come as split-K slices (decode sizes), added in slice order
+// before it joins the sum.
 #include "moe_internal.h"
 
 namespace moe {
@@ -15,7 +17,7 @@ template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ pair_pos,
-                                                      const float* __restrict__ ysh,
+                                                      const float* __restrict__ ysh, int parts,
                                                       uint16_t* __restrict__ y, int64_t T, int H) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of y
   const int per_row = H / 4;
@@ -33,7 +35,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
   for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const float4*>(o + (size_t)pp[j] * H + c);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (ysh) s = *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c);
+  if (ysh) {
+    const float* p = ysh + (size_t)t * H + c;
+    const size_t stride = (size_t)T * H;
+    s = *reinterpret_cast<const float4*>(p);
+    for (int i = 1; i < parts; ++i) {
+      const float4 b = *reinterpret_cast<const float4*>(p + i * stride);
+      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+    }
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -51,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* o, const float* topk_w, const int32_t* pair_pos,
-                          const float* ysh, uint16_t* y, int64_t T, int H, int k,
+                          const float* ysh, int ysh_parts, uint16_t* y, int64_t T, int H, int k,
                           hipStream_t st) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
@@ -59,7 +69,7 @@ hipError_t launch_combine(const float* o, const float* topk_w, const int32_t* pa
 #define MOE_COMBINE(KK)                                                                      \
   case KK:                                                                                   \
     hipLaunchKernelGGL((combine_kernel<KK>), grid, dim3(256), 0, st, o, topk_w, pair_pos, ysh, \
-                       y, T, H);                                                             \
+                       ysh_parts, y, T, H);                                                  \
     break;
   switch (k) {
     MOE_COMBINE(1) MOE_COMBINE(2) MOE_COMBINE(3) MOE_COMBINE(4)

@@ -126,6 +126,22 @@ constexpr int kMaxExperts = 512;      // largest expert count a configuration ma
 hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* q,
                             uint8_t* scale, hipStream_t st);
 
+// Decode-sized shared expert carried by the routing launches of moe_layer
+// (score routing through the split-K router, shared_split_ok(T, H, I), and
+// P <= kFusedMaxPairs): the router launch also runs the split-K up
+// projection, the top-k launch adds its slices and applies the clamped
+// SwiGLU into h, the permutation launch runs the split-K down projection into
+// part, and the combine adds the I / 512 down slices.  One stream, no fork.
+struct SharedFused {
+  const uint16_t* w1;   // [I, H] bf16
+  const uint16_t* w3;   // [I, H] bf16
+  const uint16_t* w2;   // [H, I] bf16
+  uint16_t* h;          // [M, I] bf16
+  float* part;          // shared_part_floats(M, H, I) floats
+  int M, H, I;
+  float limit;
+};
+
 // logits[t, e] = sum_h x[t, h] * wg[e, h]  (bf16 in, fp32 out)
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logits, int64_t T,
                               int H, int E, hipStream_t st);
@@ -136,9 +152,11 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wg, float* logi
 constexpr int kRouterSplits = 8;
 int router_splits(int64_t T, int H);
 // With q (may be null) the same launch also quantizes x to q / scale (as
-// launch_quant_act).
+// launch_quant_act); with sf (may be null) it also runs the shared expert's
+// split-K up projection into sf->part.
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wg, float* partial, int64_t T,
-                                 int H, int E, uint8_t* q, uint8_t* scale, hipStream_t st);
+                                 int H, int E, uint8_t* q, uint8_t* scale, const SharedFused* sf,
+                                 hipStream_t st);
 // Large batches (T >= 256, H % 64 == 0, E % 128 == 0): the bf16 tile GEMM
 // with K split router_tile_splits(T, H, E) ways (1 = no split), partial sums
 // partial[ks][t][e].
@@ -147,10 +165,12 @@ hipError_t launch_router_tile_split(const uint16_t* x, const uint16_t* wg, float
                                     int64_t T, int H, int E, int splits, hipStream_t st);
 
 // Scores + top-k from logits given as `splits` partial sums [splits][T][E]
-// (added in split order); logits_out (or NULL) receives their sum.
+// (added in split order); logits_out (or NULL) receives their sum.  With sf
+// (may be null) the same launch also turns the shared expert's up slices in
+// sf->part into sf->h.
 hipError_t launch_score_topk(const float* logits, int splits, float* logits_out, const float* bias,
                              int64_t T, int E, int k, float route_scale, int32_t* topk_idx,
-                             float* topk_w, hipStream_t st);
+                             float* topk_w, const SharedFused* sf, hipStream_t st);
 
 hipError_t launch_hash_route(const int64_t* token_ids, int64_t T, int E, int k,
                              float route_scale, uint64_t seed, int32_t* topk_idx, float* topk_w,
@@ -164,11 +184,13 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t P, int E, int32_t* ex
                           int32_t* mtile_off, hipStream_t st);
 
 // Permutation + m-tile prefix (tiles of bm pairs) of a small batch
-// (P <= kFusedMaxPairs, E <= 512) in one workgroup.
+// (P <= kFusedMaxPairs, E <= 512) in one workgroup; with sf (may be null)
+// the launch's other workgroups run the shared expert's split-K down
+// projection (sf->h x w2^T) into sf->part.
 constexpr int kFusedMaxPairs = 2048;
 hipError_t launch_perm_fused(const int32_t* topk_idx, int P, int E, int bm, int32_t* offsets,
                              int32_t* sorted_pairs, int32_t* pair_pos, int32_t* mtile_off,
-                             hipStream_t st);
+                             const SharedFused* sf, hipStream_t st);
 
 // Tile prefix of the grouped GEMMs: mtile_off[e] = sum_{e'<e} ceil(n_e'/bm).
 hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int32_t* mtile_off,
@@ -212,15 +234,23 @@ hipError_t launch_cast_fp8(const uint8_t* w, const uint8_t* ws, uint8_t* q, uint
                            int64_t rows, int K, hipStream_t st);
 
 // Shared expert (bf16): h = bf16(clamped_swiglu(x w1^T, x w3^T)) [T, I];
-// ysh = h w2^T [T, H] fp32.
+// ysh = h w2^T [T, H] fp32.  `part` holds shared_part_floats(T, H, I) floats
+// of split-K partial sums (decode-sized batches; 0 floats, and unused,
+// otherwise).  shared_split_ok: T <= 64, H and I multiples of the K slice.
+constexpr int kSharedSplitK = 512;
+bool shared_split_ok(int64_t T, int H, int I);
+int64_t shared_part_floats(int64_t T, int H, int I);
 hipError_t launch_shared_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
-                            uint16_t* h, int64_t T, int H, int I, float limit, hipStream_t st);
-hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, int64_t T,
-                              int H, int I, hipStream_t st);
+                            uint16_t* h, float* part, int64_t T, int H, int I, float limit,
+                            hipStream_t st);
+hipError_t launch_shared_down(const uint16_t* h, const uint16_t* w2, float* ysh, float* part,
+                              int64_t T, int H, int I, hipStream_t st);
 
-// y[t] = bf16(sum_j w[t,j] * o[pair_pos[t*k+j]] + ysh[t]); o fp32 [P, H].
+// y[t] = bf16(sum_j w[t,j] * o[pair_pos[t*k+j]] + ysh[t]); o fp32 [P, H];
+// ysh (may be null) given as ysh_parts slices of T * H floats, added in
+// slice order.
 hipError_t launch_combine(const float* o, const float* topk_w, const int32_t* pair_pos,
-                          const float* ysh, uint16_t* y, int64_t T, int H, int k,
+                          const float* ysh, int ysh_parts, uint16_t* y, int64_t T, int H, int k,
                           hipStream_t st);
 
 }  // namespace moe

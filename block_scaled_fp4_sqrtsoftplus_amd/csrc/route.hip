@@ -18,6 +18,7 @@
 //              ranking equal experts among lanes with a ballot), so the
 //              result is deterministic and needs no atomics on positions.
 #include "moe_internal.h"
+#include "shared_splitk.h"
 
 namespace moe {
 
@@ -37,14 +38,29 @@ __device__ __forceinline__ uint32_t key_order(float k) {
 // so each lane evaluates at most two scores (the double-precision chain is
 // the kernel's latency); each wave selects its own top k, and wave 0 selects
 // the token's top k from the 4k candidates -- the same order, since the
-// token's top k is among the union of the waves' top k.
+// token's top k is among the union of the waves' top k.  Workgroups from T
+// on (a decode-sized layer with the shared expert) finish the shared
+// expert's up projection instead: slices summed in order, clamped SwiGLU.
+struct SharedSwigluArgs {
+  const float* part;
+  uint16_t* h;
+  int S, M, I;
+  float limit;
+};
+
 __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict__ logits,
                                                          int splits, float* __restrict__ logits_out,
                                                          const float* __restrict__ bias,
                                                          int64_t T, int E, int k,
                                                          float route_scale,
                                                          int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w) {
+                                                         float* __restrict__ topk_w,
+                                                         SharedSwigluArgs sh) {
+  if ((int64_t)blockIdx.x >= T) {
+    shared_swiglu_body(sh.part, sh.S, sh.M, sh.I, sh.limit, sh.h,
+                       (int)(blockIdx.x - T) * 256 + (int)threadIdx.x);
+    return;
+  }
   __shared__ uint32_t cand_key[4][8];
   __shared__ int32_t cand_e[4][8];
   __shared__ float cand_s[4][8];
@@ -132,10 +148,16 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
 
 hipError_t launch_score_topk(const float* logits, int splits, float* logits_out, const float* bias,
                              int64_t T, int E, int k, float route_scale, int32_t* topk_idx,
-                             float* topk_w, hipStream_t st) {
+                             float* topk_w, const SharedFused* sf, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)T), dim3(256), 0, st, logits, splits,
-                     logits_out, bias, T, E, k, route_scale, topk_idx, topk_w);
+  SharedSwigluArgs sh{};
+  int64_t extra = 0;
+  if (sf) {
+    sh = SharedSwigluArgs{sf->part, sf->h, sf->H / kSharedSplitK, sf->M, sf->I, sf->limit};
+    extra = ((int64_t)sf->M * (sf->I / 4) + 255) / 256;
+  }
+  hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)(T + extra)), dim3(256), 0, st, logits,
+                     splits, logits_out, bias, T, E, k, route_scale, topk_idx, topk_w, sh);
   return hipGetLastError();
 }
 
@@ -383,16 +405,35 @@ hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int3
 // four.  Same result as the multi-kernel path: counts come from LDS
 // histograms, and the scatter keeps pair order within each expert (wave w
 // owns the w-th contiguous chunk of pairs; its base per expert is the sum of
-// the lower chunks' counts).
+// the lower chunks' counts).  Workgroups from 1 on (a decode-sized layer with
+// the shared expert) run its split-K down projection: 128 weight rows (four
+// row waves) x one 512-slice of I each.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;
+
+struct SharedDownArgs {
+  const uint16_t* h;
+  const uint16_t* w2;
+  float* part;
+  int M, H, I;
+  int blocks;
+};
 
 __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
     const int32_t* __restrict__ topk_idx, int P, int E, int bm, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ mtile_off) {
-  __shared__ int32_t sel[kFusedMaxPairs];
-  __shared__ int32_t wcnt[kFusedWaves][512];   // per-wave counts, then per-wave bases
+    int32_t* __restrict__ mtile_off, SharedDownArgs sh) {
+  // 64 KB: the permutation's pair and count arrays (40 KB), or the split-K token slice
+  __shared__ uint4 lds[64][64];
+  if (blockIdx.x > 0) {
+    const int b = blockIdx.x - 1, nbx = sh.H / shared_splitk_rows<EPI_F32, 4>();
+    shared_splitk_body<EPI_F32, kFusedWaves, 4>(sh.h, sh.w2, nullptr, sh.part, sh.M, sh.H, sh.I,
+                                                b % nbx, b / nbx, lds);
+    return;
+  }
+  int32_t* sel = reinterpret_cast<int32_t*>(&lds[0][0]);   // [kFusedMaxPairs]
+  // [kFusedWaves][512]: per-wave counts, then per-wave bases
+  int32_t (*wcnt)[512] = reinterpret_cast<int32_t (*)[512]>(sel + kFusedMaxPairs);
   __shared__ int32_t tot[8];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -452,9 +493,14 @@ __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
 
 hipError_t launch_perm_fused(const int32_t* topk_idx, int P, int E, int bm, int32_t* offsets,
                              int32_t* sorted_pairs, int32_t* pair_pos, int32_t* mtile_off,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(perm_fused_kernel, dim3(1), dim3(kFusedWaves * 64), 0, st, topk_idx, P, E,
-                     bm, offsets, sorted_pairs, pair_pos, mtile_off);
+                             const SharedFused* sf, hipStream_t st) {
+  SharedDownArgs sh{};
+  if (sf) {
+    sh = SharedDownArgs{sf->h, sf->w2, sf->part, sf->M, sf->H, sf->I,
+                        (sf->H / shared_splitk_rows<EPI_F32, 4>()) * (sf->I / kSharedSplitK)};
+  }
+  hipLaunchKernelGGL(perm_fused_kernel, dim3((unsigned)(1 + sh.blocks)), dim3(kFusedWaves * 64), 0,
+                     st, topk_idx, P, E, bm, offsets, sorted_pairs, pair_pos, mtile_off, sh);
   return hipGetLastError();
 }
 

@@ -51,6 +51,17 @@ def check_routing_valid(r, T, k, E):
     ("tiny", 20, dict(n_experts=512, top_k=8, hidden=256, inter=128)),   # largest E and k
     ("decode", 5, dict(n_experts=12)),
     ("decode", 300, dict(hidden=1024, inter=1024, n_experts=4, top_k=2, shared=True)),
+    # decode-sized shared expert through the split-K kernels (T <= 64, H and I
+    # multiples of 512) on the side stream: ragged T, a full 64-token batch,
+    # a single token
+    ("decode", 37, dict(hidden=1024, inter=512, n_experts=8, top_k=2, shared=True)),
+    ("decode", 64, dict(hidden=1536, inter=1024, n_experts=8, top_k=2, shared=True)),
+    ("decode", 1, dict(hidden=512, inter=512, n_experts=4, top_k=2, shared=True)),
+    # ... and inside the routing launches (split-K router: H in {2048, 4096,
+    # 8192}): three, one and four down slices, ragged / full / single batches
+    ("decode", 37, dict(hidden=2048, inter=1536, n_experts=16, top_k=4, shared=True)),
+    ("decode", 64, dict(hidden=2048, inter=512, n_experts=8, top_k=2, shared=True)),
+    ("decode", 1, dict(hidden=2048, inter=2048, n_experts=8, top_k=8, shared=True)),
 ])
 def test_layer_parity_small(shape):
     name, tokens, over = shape
