@@ -100,29 +100,6 @@ __device__ __forceinline__ v4f mfma_fp8_fp8(const uint4& a0, const uint4& a1, co
   return acc;
 }
 
-// Maps the workgroup to (n_tile, expert, m0); returns false when idle.
-__device__ __forceinline__ bool map_tile(const ExpertGemmArgs& p, int mt_max, int n_tiles, int bm,
-                                         int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int w = (b & 7) * (G >> 3) + (b >> 3);
-  n_tile = w / mt_max;
-  const int mt = w - n_tile * mt_max;
-  if (n_tile >= n_tiles) return false;
-  const int total = p.mtile_off[p.E];
-  if (mt >= total) return false;
-  int lo = 0, hi = p.E;  // mtile_off[lo] <= mt < mtile_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
-  }
-  e = lo;
-  m0 = (mt - p.mtile_off[e]) * bm;
-  off_e = p.expert_offsets[e];
-  n_e = p.expert_offsets[e + 1] - off_e;
-  return true;
-}
-
 // The MT MFMAs of one weight tile in a K step of the generic kernel (FP4
 // weights: A = 16 bytes, cbsz 4; FP8 weights: A = 32 bytes, cbsz 0), from one
 // asm statement; the last of a step (the _g variants) closes it with 32 wait
@@ -175,7 +152,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
   __shared__ float red[4][BM];
 
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile(p, mt_max, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, BM, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -418,7 +395,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
                                                                     int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -612,7 +589,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream8(ExpertGemmAr
                                                                      int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;

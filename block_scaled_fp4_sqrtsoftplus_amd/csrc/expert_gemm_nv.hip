@@ -53,27 +53,6 @@ __device__ __forceinline__ h8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
   return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ bool map_tile_nv(const ExpertGemmArgs& p, int mt_max, int n_tiles,
-                                            int bm, int& n_tile, int& e, int& m0, int& off_e, int& n_e) {
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int w = (b & 7) * (G >> 3) + (b >> 3);   // XCD-aware: consecutive ids per XCD
-  n_tile = w / mt_max;
-  const int mt = w - n_tile * mt_max;
-  if (n_tile >= n_tiles) return false;
-  if (mt >= p.mtile_off[p.E]) return false;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
-  }
-  e = lo;
-  m0 = (mt - p.mtile_off[e]) * bm;
-  off_e = p.expert_offsets[e];
-  n_e = p.expert_offsets[e + 1] - off_e;
-  return true;
-}
-
 }  // namespace
 
 // LDS row stride of the staged scale lines: 256 bytes (K = 4096) + 16, so
@@ -92,7 +71,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
                                                                 int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_nv(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -338,7 +317,7 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
   __shared__ __attribute__((aligned(16))) uint8_t bsl[kNvM][32];
   __shared__ float red[8][kNvM];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_nv(p, mt_max, n_tiles, kNvM, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, kNvM, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;

@@ -107,28 +107,6 @@ __device__ __forceinline__ v8i act_operand(const v4u& b0, const v4u& b1) {
   return r;
 }
 
-__device__ __forceinline__ bool map_tile_w4(const ExpertGemmArgs& p, int mt_max, int n_tiles,
-                                            int bm, int& n_tile, int& e, int& m0, int& off_e,
-                                            int& n_e) {
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int w = (b & 7) * (G >> 3) + (b >> 3);   // XCD-aware: consecutive ids per XCD
-  n_tile = w / mt_max;
-  const int mt = w - n_tile * mt_max;
-  if (n_tile >= n_tiles) return false;
-  if (mt >= p.mtile_off[p.E]) return false;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.mtile_off[mid] <= mt) lo = mid; else hi = mid;
-  }
-  e = lo;
-  m0 = (mt - p.mtile_off[e]) * bm;
-  off_e = p.expert_offsets[e];
-  n_e = p.expert_offsets[e + 1] - off_e;
-  return true;
-}
-
 constexpr int kW4ScaleB = 127 + 9;        // E8M0 2^9: undoes the 2^-9 of the INT4 bytes
 
 }  // namespace
@@ -144,7 +122,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
                                                                    int n_tiles) {
   __shared__ float red[4][16];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_w4(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -352,7 +330,7 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
   __shared__ __attribute__((aligned(16))) uint8_t bsl[kW4M][32];
   __shared__ float red[8][kW4M];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_tile_w4(p, mt_max, n_tiles, kW4M, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile(p, mt_max, n_tiles, kW4M, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;

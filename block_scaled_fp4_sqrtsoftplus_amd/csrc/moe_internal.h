@@ -217,6 +217,40 @@ struct ExpertGemmArgs {
                              // (NVFP4 and W4AFP8 have launchers of their own)
 };
 
+// Grouped-GEMM workgroup -> (n_tile, expert, m0) for grids of n_tiles x
+// mt_max workgroups (XCD-aware: workgroup b runs on XCD b % 8, and each
+// XCD takes a contiguous run of tiles); false when the workgroup is idle.
+// The expert of m-tile mt is the largest e < E with mtile_off[e] <= mt: the
+// number of prefix entries at most mt, less one (an expert with no tiles
+// shares its entry with the next, so that index is never an empty expert).
+// Each lane of the wave compares up to nine entries (E <= 512), all loads
+// issued at once: one round of loads instead of a chain of dependent ones
+// before the weight stream can start.  Wave-uniform control flow required.
+__device__ __forceinline__ bool map_expert_tile(const ExpertGemmArgs& p, int mt_max, int n_tiles,
+                                                int bm, int& n_tile, int& e, int& m0, int& off_e,
+                                                int& n_e) {
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int w = (b & 7) * (G >> 3) + (b >> 3);
+  n_tile = w / mt_max;
+  const int mt = w - n_tile * mt_max;
+  if (n_tile >= n_tiles) return false;
+  const int lane = threadIdx.x & 63;
+  const int total = p.mtile_off[p.E];
+  int v[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) v[j] = p.mtile_off[min(lane + 64 * j, p.E)];
+  if (mt >= total) return false;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) cnt += __popcll(__ballot(lane + 64 * j <= p.E && v[j] <= mt));
+  e = cnt - 1;
+  m0 = (mt - __builtin_amdgcn_readfirstlane(p.mtile_off[e])) * bm;
+  off_e = p.expert_offsets[e];
+  n_e = p.expert_offsets[e + 1] - off_e;
+  return true;
+}
+
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
 hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
