@@ -59,6 +59,25 @@ def test_workspace_sizes():
     assert lib.moe_workspace_size(ctypes.byref(c), 7) == 0
 
 
+def test_layer_workspace_holds_shared_split_partials():
+    # decode-sized batches (T <= 64, H and I multiples of 512) add the shared
+    # expert's split-K partial sums: max(H/512 * T * 2I, I/512 * T * H) floats
+    base = dict(n_experts=8, top_k=2)
+    for T, H, I in [(64, 4096, 2048), (1, 2048, 512), (37, 1024, 1536)]:
+        with_part = lib.moe_workspace_size(ctypes.byref(_cfg(tokens=T, hidden=H, inter=I, **base)),
+                                           moe.OP_LAYER)
+        # the same sizes with I = 384 (not a multiple of 512) carve no partials
+        no_part = lib.moe_workspace_size(ctypes.byref(_cfg(tokens=T, hidden=H, inter=I - 128, **base)),
+                                         moe.OP_LAYER)
+        part = max(H // 512 * T * 2 * I, I // 512 * T * H) * 4
+        assert with_part >= part
+        assert with_part - no_part >= part - 256 * 64   # I - 128 shrinks the other buffers a little
+    # 65 tokens: the side-stream kernels, no partials
+    a = lib.moe_workspace_size(ctypes.byref(_cfg(tokens=65, **base)), moe.OP_LAYER)
+    b = lib.moe_workspace_size(ctypes.byref(_cfg(tokens=65, inter=1920, **base)), moe.OP_LAYER)
+    assert a - b < 8 * 64 * 4096 * 4
+
+
 @pytest.mark.parametrize("field,value", [
     ("tokens", -1), ("hidden", 0), ("hidden", 200), ("hidden", 32768), ("inter", 64),
     ("n_experts", 0), ("n_experts", 513), ("top_k", 0), ("top_k", 9), ("route_mode", 3),
