@@ -236,14 +236,15 @@ __device__ __forceinline__ bool map_expert_tile(const ExpertGemmArgs& p, int mt_
   const int mt = w - n_tile * mt_max;
   if (n_tile >= n_tiles) return false;
   const int lane = threadIdx.x & 63;
-  const int total = p.mtile_off[p.E];
   int v[9];
 #pragma unroll
   for (int j = 0; j < 9; ++j) v[j] = p.mtile_off[min(lane + 64 * j, p.E)];
-  if (mt >= total) return false;
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < 9; ++j) cnt += __popcll(__ballot(lane + 64 * j <= p.E && v[j] <= mt));
+  // all E + 1 entries at most mt: mt is past the last tile (mtile_off[E] is
+  // the tile count), so the workgroup is idle -- no separate load of it
+  if (cnt > p.E) return false;
   e = cnt - 1;
   m0 = (mt - __builtin_amdgcn_readfirstlane(p.mtile_off[e])) * bm;
   off_e = p.expert_offsets[e];
