@@ -406,8 +406,10 @@ hipError_t launch_tile_prefix(const int32_t* expert_offsets, int E, int bm, int3
 // histograms, and the scatter keeps pair order within each expert (wave w
 // owns the w-th contiguous chunk of pairs; its base per expert is the sum of
 // the lower chunks' counts).  Workgroups from 1 on (a decode-sized layer with
-// the shared expert) run its split-K down projection: 128 weight rows (four
-// row waves) x one 512-slice of I each.
+// the shared expert) run its split-K down projection: 64 weight rows (two
+// row waves, eight K waves each) x one 512-slice of I per workgroup, 256
+// workgroups at H = 4096, I = 2048 (four row waves and 128 workgroups:
+// 0.5 us slower).
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;
 
@@ -426,8 +428,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void perm_fused_kernel(
   // 64 KB: the permutation's pair and count arrays (40 KB), or the split-K token slice
   __shared__ uint4 lds[64][64];
   if (blockIdx.x > 0) {
-    const int b = blockIdx.x - 1, nbx = sh.H / shared_splitk_rows<EPI_F32, 4>();
-    shared_splitk_body<EPI_F32, kFusedWaves, 4>(sh.h, sh.w2, nullptr, sh.part, sh.M, sh.H, sh.I,
+    const int b = blockIdx.x - 1, nbx = sh.H / shared_splitk_rows<EPI_F32, 2>();
+    shared_splitk_body<EPI_F32, kFusedWaves, 2>(sh.h, sh.w2, nullptr, sh.part, sh.M, sh.H, sh.I,
                                                 b % nbx, b / nbx, lds);
     return;
   }
@@ -497,7 +499,7 @@ hipError_t launch_perm_fused(const int32_t* topk_idx, int P, int E, int bm, int3
   SharedDownArgs sh{};
   if (sf) {
     sh = SharedDownArgs{sf->h, sf->w2, sf->part, sf->M, sf->H, sf->I,
-                        (sf->H / shared_splitk_rows<EPI_F32, 4>()) * (sf->I / kSharedSplitK)};
+                        (sf->H / shared_splitk_rows<EPI_F32, 2>()) * (sf->I / kSharedSplitK)};
   }
   hipLaunchKernelGGL(perm_fused_kernel, dim3((unsigned)(1 + sh.blocks)), dim3(kFusedWaves * 64), 0,
                      st, topk_idx, P, E, bm, offsets, sorted_pairs, pair_pos, mtile_off, sh);
