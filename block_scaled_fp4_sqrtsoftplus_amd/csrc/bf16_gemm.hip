@@ -313,6 +313,15 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
   *reinterpret_cast<float4*>(y + 4 * (size_t)i) = a;
 }
 
+// Shared-expert up projection riding in the router launch (blocks = 0: none).
+struct SharedUpArgs {
+  const uint16_t* w1;
+  const uint16_t* w3;
+  float* part;
+  int I;
+  int blocks;
+};
+
 // ---------------------------------------------------------------------------
 // Router logits of a small batch (M <= 64 tokens): the gate matrix is only
 // E x H bf16 (2 MB at E = 256), so the whole read must be in flight at once.
@@ -327,15 +336,6 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 // workgroups after the router's run the shared expert's split-K up
 // projection (it reads the same x), which then needs no launch of its own.
 // ---------------------------------------------------------------------------
-// Shared-expert up projection riding in the router launch (blocks = 0: none).
-struct SharedUpArgs {
-  const uint16_t* w1;
-  const uint16_t* w3;
-  float* part;
-  int I;
-  int blocks;
-};
-
 template <int MT, int STEPS>
 __global__ __launch_bounds__(512) void router_splitk_kernel(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ W,
