@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <new>
 
@@ -157,7 +158,8 @@ struct SideStream {
 };
 SideStream g_side[64];
 
-// Batches from which moe_layer starts the shared expert before routing.
+// Batches from which moe_layer starts the shared expert early: before the
+// top-k and permutation (score routing) or before quantization (hash).
 constexpr int64_t kEarlyForkTokens = 256;
 
 moe_status side_stream(SideStream*& out) {
@@ -224,9 +226,13 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
                          float* logits_out, const moe_routing& r, const RouteWs& ws,
                          hipStream_t st, int32_t* mtile_off = nullptr, bool* tiles_done = nullptr,
                          uint8_t* xq = nullptr, uint8_t* xs = nullptr,
-                         const SharedFused* sf = nullptr) {
+                         const SharedFused* sf = nullptr,
+                         const std::function<moe_status()>* after_router = nullptr) {
   const int64_t T = c.tokens, P = T * c.top_k;
   if (tiles_done) *tiles_done = false;
+  // called once the router GEMM (or the hash routing) is enqueued
+  auto routed = [&]() -> moe_status { return after_router ? (*after_router)() : MOE_OK; };
+  moe_status rs;
   // the shared expert rides only in the split-K router / fused permutation launches
   if (sf && !(c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && !logits_in &&
               router_tile_splits(T, c.hidden, c.n_experts) == 1 &&
@@ -235,22 +241,27 @@ moe_status enqueue_route(const moe_config& c, const uint16_t* x, const uint16_t*
   if (c.route_mode == MOE_ROUTE_HASH) {
     MOE_TRY(launch_hash_route(ids, T, c.n_experts, c.top_k, c.route_scale, c.hash_seed,
                               r.topk_idx, r.topk_w, st));
+    if ((rs = routed()) != MOE_OK) return rs;
   } else if (logits_in) {
+    if ((rs = routed()) != MOE_OK) return rs;
     MOE_TRY(launch_score_topk(logits_in, 1, logits_out, bias, T, c.n_experts, c.top_k,
                               c.route_scale, r.topk_idx, r.topk_w, nullptr, st));
   } else if (router_tile_splits(T, c.hidden, c.n_experts) > 1) {
     const int ks = router_tile_splits(T, c.hidden, c.n_experts);
     MOE_TRY(launch_router_tile_split(x, wg, ws.logits, T, c.hidden, c.n_experts, ks, st));
+    if ((rs = routed()) != MOE_OK) return rs;
     MOE_TRY(launch_score_topk(ws.logits, ks, logits_out, bias, T, c.n_experts, c.top_k,
                               c.route_scale, r.topk_idx, r.topk_w, nullptr, st));
   } else if (router_splits(T, c.hidden) > 1) {
     MOE_TRY(launch_router_partial(x, wg, ws.logits, T, c.hidden, c.n_experts, xq, xs, sf, st));
+    if ((rs = routed()) != MOE_OK) return rs;
     MOE_TRY(launch_score_topk(ws.logits, router_splits(T, c.hidden), logits_out, bias, T,
                               c.n_experts, c.top_k, c.route_scale, r.topk_idx, r.topk_w, sf,
                               st));
   } else {
     float* dst = logits_out ? logits_out : ws.logits;
     MOE_TRY(launch_router_gemm(x, wg, dst, T, c.hidden, c.n_experts, st));
+    if ((rs = routed()) != MOE_OK) return rs;
     MOE_TRY(launch_score_topk(dst, 1, nullptr, bias, T, c.n_experts, c.top_k, c.route_scale,
                               r.topk_idx, r.topk_w, nullptr, st));
   }
@@ -486,9 +497,13 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   // Small batches fork it once routing is enqueued, so that it overlaps the
   // bandwidth-bound expert GEMMs rather than the latency-bound routing
   // kernels (forking first cost 2% at T = 64); batches of at least
-  // kEarlyForkTokens fork it first, where its GEMMs are long enough to fill
-  // the GPU the routing kernels leave idle (1.6% less layer time at
-  // T = 32768, the same at T = 4096).
+  // kEarlyForkTokens fork it early, where its GEMMs are long enough to fill
+  // the GPU the routing kernels leave idle: hash routing before the
+  // quantization (1.6% less layer time at T = 32768 than forking after
+  // routing), score routing right after the router GEMM is enqueued -- forked
+  // before it, the shared up projection's workgroups took the GPU first and
+  // the router GEMM, on the critical path, waited for slots (184 us at
+  // T = 4096; the layer 1.5% slower).
   const bool quant_in_router =
       c.route_mode == MOE_ROUTE_SQRTSOFTPLUS && router_splits(c.tokens, c.hidden) > 1;
   const bool fused_shared = shared && quant_in_router &&
@@ -520,14 +535,18 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   };
   const bool side_shared = shared && !fused_shared;
   const bool early_fork = side_shared && c.tokens >= kEarlyForkTokens;
-  if (early_fork && (s = fork_shared()) != MOE_OK) return s;
+  // score routing forks right after the router GEMM is enqueued, hash routing
+  // before the quantization
+  const bool fork_after_router = early_fork && c.route_mode == MOE_ROUTE_SQRTSOFTPLUS;
+  if (early_fork && !fork_after_router && (s = fork_shared()) != MOE_OK) return s;
+  const std::function<moe_status()> fork_fn = fork_shared;
   // small score-routed batches quantize x inside the split-K router launch
   if (!quant_in_router) MOE_TRY(launch_quant_act(x, c.tokens, c.hidden, l.xq, l.xs, st));
   bool tiles_done = false;
   if ((s = enqueue_route(c, x, w_gate, bias, token_ids, nullptr, nullptr, r, l.route, st,
                          l.ffn.mtile_off, &tiles_done, quant_in_router ? l.xq : nullptr,
-                         quant_in_router ? l.xs : nullptr,
-                         fused_shared ? &sf : nullptr)) != MOE_OK)
+                         quant_in_router ? l.xs : nullptr, fused_shared ? &sf : nullptr,
+                         fork_after_router ? &fork_fn : nullptr)) != MOE_OK)
     return s;
   if (side_shared && !early_fork && (s = fork_shared()) != MOE_OK) return s;
   if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,
