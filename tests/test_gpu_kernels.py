@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import splitmix_construct
 import synth
 from oracle import formats, quant, route as oroute, ffn
 from gpu_util import config, dev, dev_bf16, device_inputs, host, near_tie_tokens, norm_err
@@ -100,15 +101,22 @@ def test_route_empty():
     assert np.all(host(g["expert_offsets"]) == 0)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hash"])
-def test_hash_route_bit_exact(name):
+@pytest.mark.parametrize("name,E", [("tiny", 24), ("tiny", 384), ("hash", None)])
+def test_hash_route_bit_exact(name, E):
     wl = synth.WORKLOADS[name]
-    if name == "tiny":
-        wl = wl.replace(mode="hash", n_experts=24, top_k=6)   # 24: not a power of two
+    if E is not None:
+        wl = wl.replace(mode="hash", n_experts=E, top_k=6)   # not powers of two
     ids = synth.make_inputs(wl.replace(n_experts=1), experts_only=[])["token_ids"]
+    if E is not None:
+        # tokens whose streams put a draw exactly at, and just below, the
+        # rejection limit 2**64 - (2**64 mod E), and one at the top mid-stream
+        cases = splitmix_construct.rejection_tokens(wl.seed, E, 6)
+        ids = np.concatenate([ids, np.array([c[0] for c in cases], np.int64)])
     ref = oroute.route(k=wl.top_k, route_scale=wl.route_scale, mode="hash", token_ids=ids,
                        seed=wl.seed, n_experts=wl.n_experts)
-    cfg = config(moe, wl, route_mode=moe.ROUTE_HASH)
+    if E is not None:
+        assert ref["topk_idx"][-len(cases):].tolist() == [c[1] for c in cases]
+    cfg = config(moe, wl, route_mode=moe.ROUTE_HASH, tokens=len(ids))
     g = moe.route(cfg, token_ids=dev(ids))
     torch.cuda.synchronize()
     _check_routing(g, ref)

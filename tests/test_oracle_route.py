@@ -1,16 +1,22 @@
 """Pins of the oracle's routing: sqrtsoftplus against high-precision values
 (mpmath) and its closed-form limits, top-k against brute force with forced
 ties, the weights' normalisation, SplitMix64 against its published outputs,
-hash routing properties, and the permutation against a library stable sort."""
+hash routing properties and its rejection rule on tokens constructed to reach
+it, the router logits against exact integer arithmetic, exact rational dot
+products and torch's float64 matmul, and the permutation against a library
+stable sort."""
 
 import itertools
 import os
+from fractions import Fraction
 
 import mpmath
 import numpy as np
 import pytest
+import torch
 
-from oracle import route
+import splitmix_construct
+from oracle import formats, route
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -126,16 +132,104 @@ def test_hash_route_properties():
     assert chi2 < 255 + 5 * np.sqrt(2 * 255)
 
 
-def test_hash_rejection_for_non_power_of_two():
-    # E = 384: r >= 2**64 - (2**64 mod 384) is rejected; with a state that
-    # starts just below such an output the rule is exercised on a constructed stream
-    E = 384
-    limit = (1 << 64) - ((1 << 64) % E)
-    outs, _ = route.splitmix64_stream(12345, 5000)
-    assert all(o < (1 << 64) for o in outs)
-    e = route.hash_route_token(7, 3, E, 6)
-    assert len(set(e)) == 6 and all(0 <= v < E for v in e)
-    assert limit % E == 0
+@pytest.mark.parametrize("E,seed", [(384, 1004), (384, 1005), (24, 1001), (200, 7)])
+def test_hash_rejection_constructed(E, seed):
+    # tokens whose streams hold a draw at the limit 2**64 - (2**64 mod E), one
+    # below it, and one at 2**64 - 1 mid-stream (built by inverting SplitMix64,
+    # tests/splitmix_construct.py): the oracle must drop the first and the
+    # third and keep the second; a > for >= or a limit off by one fails
+    for tid, expect, what in splitmix_construct.rejection_tokens(seed, E, 6):
+        got = route.hash_route_token(tid & route.MASK64, seed, E, 6)
+        assert got == expect, what
+    # the same tokens through the vectorised route
+    cases = splitmix_construct.rejection_tokens(seed, E, 6)
+    idx, w = route.hash_route(np.array([c[0] for c in cases], np.int64), seed, E, 6)
+    assert idx.tolist() == [c[1] for c in cases]
+    assert np.all(w == np.float32(0.25))
+
+
+def test_hash_construction_round_trip():
+    # the inverse used above agrees with the published outputs' generator
+    rng = np.random.default_rng(26)
+    for _ in range(200):
+        v = int(rng.integers(0, 1 << 63)) * 2 + int(rng.integers(0, 2))
+        seed = int(rng.integers(0, 1 << 32))
+        i = int(rng.integers(0, 5))
+        tid = splitmix_construct.token_with_draw(seed, i, v)
+        out, _ = route.splitmix64_stream(splitmix_construct.start_state(seed, tid), i + 1)
+        assert out[i] == v
+
+
+def _bf16_bits_exact(u):
+    """bf16 bit pattern -> (integer significand, power of two), decoded from
+    the bits by hand (sign, 8-bit exponent with bias 127, 7-bit fraction)."""
+    u = int(u)
+    sign = -1 if u & 0x8000 else 1
+    ex = (u >> 7) & 0xFF
+    fr = u & 0x7F
+    assert ex != 0xFF
+    if ex == 0:
+        return sign * fr, -133
+    return sign * (128 + fr), ex - 134
+
+
+def _exact_dot(xr, wr):
+    """Exact dot product of two bf16 rows as a Fraction."""
+    terms = [(_bf16_bits_exact(a), _bf16_bits_exact(b)) for a, b in zip(xr, wr)]
+    lo = min(ea + eb for (_, ea), (_, eb) in terms)
+    total = sum(ma * mb << (ea + eb - lo) for (ma, ea), (mb, eb) in terms)
+    return Fraction(total) * Fraction(2) ** lo
+
+
+def test_router_logits_exact_integers():
+    # bf16 integers with dot products below 2**24: every logit is exact, and
+    # must equal the int64 product with the gate's rows (z = x Wg^T; T, E and H
+    # distinct so that a transposed operand cannot pass)
+    rng = np.random.default_rng(27)
+    T, E, H = 7, 11, 1536
+    xi = rng.integers(-9, 10, (T, H))
+    wi = rng.integers(-9, 10, (E, H))
+    z = route.router_logits(formats.bf16_encode(xi.astype(np.float64)),
+                            formats.bf16_encode(wi.astype(np.float64)))
+    assert z.dtype == np.float32 and z.shape == (T, E)
+    assert np.array_equal(z.astype(np.int64), xi @ wi.T)
+    assert np.all(np.abs(xi @ wi.T) < 2 ** 24)
+
+
+def test_router_logits_correctly_rounded():
+    # N(0,1) activations against N(0,0.02) gate rows at the full hidden size:
+    # each logit is the exact dot product rounded once to fp32, up to the
+    # float64 accumulation's own error (H * 2**-53 of sum |x w|); fp32
+    # accumulation, a truncating rounding or a dropped term exceeds this
+    rng = np.random.default_rng(28)
+    T, E, H = 4, 6, 4096
+    xu = formats.bf16_encode(rng.standard_normal((T, H)))
+    wu = formats.bf16_encode(rng.standard_normal((E, H)) * 0.02)
+    z = route.router_logits(xu, wu)
+    absdot = np.abs(formats.bf16_decode(xu)) @ np.abs(formats.bf16_decode(wu)).T
+    for t in range(T):
+        for e in range(E):
+            ex = _exact_dot(xu[t], wu[e])
+            half_ulp = Fraction(float(np.spacing(np.abs(z[t, e])))) / 2
+            slack = Fraction(H * 2.0 ** -53 * float(absdot[t, e]))
+            assert abs(Fraction(float(z[t, e])) - ex) <= half_ulp + slack, (t, e)
+
+
+def test_router_logits_library_route():
+    # torch float64 matmul of the same bf16 tensors (torch's own bf16 decode),
+    # rounded to fp32: equal except where the two float64 summation orders
+    # straddle an fp32 rounding boundary (at most 1 ulp, rarely)
+    rng = np.random.default_rng(29)
+    T, E, H = 64, 256, 4096
+    xu = formats.bf16_encode(rng.standard_normal((T, H)))
+    wu = formats.bf16_encode(rng.standard_normal((E, H)) * 0.02)
+    z = route.router_logits(xu, wu)
+    xt = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).double()
+    wt = torch.from_numpy(wu.view(np.int16)).view(torch.bfloat16).double()
+    ref = (xt @ wt.T).float().numpy()
+    diff = np.abs(z.astype(np.float64) - ref)
+    assert np.all(diff <= np.spacing(np.abs(ref)))
+    assert np.mean(diff == 0) > 0.999
 
 
 def test_permutation_vs_stable_sort():
