@@ -21,7 +21,7 @@ workload number, so that each tensor -- and each expert -- is drawn
 independently of the others and of the token count):
   x        N(0, 1) fp32 -> bf16 (round to nearest even)        [T, H]
   w_gate   N(0, 0.02) -> bf16                                   [E, H]
-  bias     skewed only: see zipf_bias                           [E] fp32
+  bias     skewed only: frozen Zipf(1.1) calibration (zipf_bias) [E] fp32
   w1, w3   uniform bytes (both nibbles uniform over 16 codes)   [E, I, H/2]
   w2       uniform bytes                                        [E, H, I/2]
   scales   E8M0 bytes 127 + uniform{exp_lo..exp_hi}             [E, N, K/32]
@@ -32,6 +32,7 @@ pre-activation standard deviation about 0.97, so the +-10 clamp is only
 touched in the tails; the tiny workload's -6..0 saturates most of them.
 """
 
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -77,12 +78,25 @@ def _bf16_bits(a32):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def zipf_bias(n_experts, rng, s=1.1, strength=0.45):
-    """Gate bias for the skewed workload: expert e gets rank r_e (a seeded
-    permutation) and bias strength * ln(r_e ** -s), so lower ranks win the
-    top-k far more often; the realised load is reported by the callers."""
-    ranks = rng.permutation(n_experts) + 1
-    return (strength * (-s) * np.log(ranks.astype(np.float64))).astype(np.float32)
+def zipf_ranks(wl: Workload):
+    """Popularity ranks 1..E of the experts (a seeded permutation) for the
+    skewed workload's Zipf target."""
+    rng = np.random.Generator(np.random.PCG64([wl.seed, 3]))
+    return rng.permutation(wl.n_experts) + 1
+
+
+ZIPF_BIAS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "zipf_bias_skewed.txt")
+
+
+def zipf_bias(wl: Workload):
+    """The skewed workload's gate bias [E] fp32, frozen in zipf_bias_skewed.txt
+    (calibrated once so that expert popularity follows Zipf(1.1) over the
+    ranks of zipf_ranks; the file's header names the script and recipe)."""
+    vals = [int(l, 16) for l in open(ZIPF_BIAS_FILE) if l.strip() and not l.startswith("#")]
+    b = np.array(vals, np.uint32).view(np.float32)
+    if len(b) != wl.n_experts:
+        raise ValueError(f"frozen Zipf bias holds {len(b)} experts, workload has {wl.n_experts}")
+    return b
 
 
 def make_inputs(wl: Workload, tokens=None, experts_only=None):
@@ -100,7 +114,7 @@ def make_inputs(wl: Workload, tokens=None, experts_only=None):
     out = {}
     out["x"] = _bf16_bits(rng(1).standard_normal((T, H), dtype=np.float32))
     out["w_gate"] = _bf16_bits(rng(2).standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
-    out["bias"] = zipf_bias(E, rng(3)) if wl.zipf_bias else None
+    out["bias"] = zipf_bias(wl) if wl.zipf_bias else None
     nexp = wl.exp_hi - wl.exp_lo + 1
 
     def draw_expert(r, n, k):
