@@ -25,7 +25,10 @@ FP4 x FP8 products have at most 7 significant bits, so these sums are exact
 or within a few float64 ulps).
 """
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 from . import formats, quant, route as route_mod
 
@@ -41,7 +44,8 @@ def clamped_swiglu(g, u, limit):
     return silu(gc) * uc
 
 
-def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_format="mxfp4"):
+def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_format="mxfp4",
+               out=None):
     """Routed experts on quantized activations.
 
     xq u8 [T, H], xs u8 [T, H/128]; routing from route.route; w dict with
@@ -52,6 +56,10 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_forma
     the nibbles are signed INT4 with [E, N, K/128] float32 scales.
     Returns dict: hq u8 [P, I], hs u8 [P, I/128], h fp32 [P, I] (before its
     quantization) and o float64 [P, H], all rows in sorted-pair order.
+    `experts` (a list of expert ids) computes only those experts' rows, the
+    others are left zero; `out` (a dict of such arrays) receives the rows in
+    place of new arrays.  Experts are independent, so callers may run
+    disjoint expert lists at once into one `out`.
     """
     off = routing["expert_offsets"]
     sp = routing["sorted_pairs"]
@@ -61,11 +69,11 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_forma
     H = w["w2"].shape[1]
     deq = {"mxfp4": quant.mxfp4_dequant, "fp8": quant.fp8_dequant,
            "nvfp4": quant.nvfp4_dequant, "w4afp8": quant.int4_dequant}[weight_format]
-    hq = np.zeros((P, I), np.uint8)
-    hs = np.zeros((P, I // 128), np.uint8)
-    hf = np.zeros((P, I), np.float32)
-    o = np.zeros((P, H), np.float64)
-    for e in range(E):
+    if out is None:
+        out = {"hq": np.zeros((P, I), np.uint8), "hs": np.zeros((P, I // 128), np.uint8),
+               "h": np.zeros((P, I), np.float32), "o": np.zeros((P, H), np.float64)}
+    hq, hs, hf, o = out["hq"], out["hs"], out["h"], out["o"]
+    for e in (range(E) if experts is None else experts):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
@@ -80,7 +88,7 @@ def expert_ffn(xq, xs, routing, w, top_k, limit=10.0, experts=None, weight_forma
         q, s = quant.act_quant(h.astype(np.float64))
         hq[lo:hi], hs[lo:hi], hf[lo:hi] = q, s, h
         o[lo:hi] = quant.act_dequant(q, s) @ W2.T
-    return {"hq": hq, "hs": hs, "h": hf, "o": o}
+    return out
 
 
 def shared_expert(x_u16, w1_u16, w3_u16, w2_u16, limit=10.0):
@@ -106,12 +114,15 @@ def combine(o, routing, ysh=None):
 
 
 def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0,
-          weight_format="mxfp4"):
+          weight_format="mxfp4", workers=1):
     """The whole MoE FFN layer on the inputs of synth.make_inputs; with
     weight_format "fp8" the routed experts run on the FP8 cast of the MXFP4
     weights (quant.fp8_experts_from_mxfp4); with "nvfp4" inp's w*_scale are
     the NVFP4 per-16 E4M3 scales of the same nibbles; with "w4afp8" the
     nibbles are INT4 codes and inp's w*_scale their float32 per-128 scales.
+
+    `workers` > 1 runs the experts on that many threads, each on its own
+    experts (the results do not depend on it).
 
     Returns dict with the routing, xq/xs, hq/hs, o, ysh (or None), y (float64)
     and y_bf16 (uint16 bit patterns)."""
@@ -125,7 +136,19 @@ def layer(inp, top_k, route_scale=1.5, limit=10.0, mode="score", hash_seed=0,
         r = route_mod.route(x, inp["w_gate"], k=top_k, bias=inp.get("bias"),
                             route_scale=route_scale)
     w = quant.fp8_experts_from_mxfp4(inp) if weight_format == "fp8" else inp
-    f = expert_ffn(xq, xs, r, w, top_k, limit, weight_format=weight_format)
+    if workers <= 1:
+        f = expert_ffn(xq, xs, r, w, top_k, limit, weight_format=weight_format)
+    else:
+        P, I, H = r["sorted_pairs"].size, w["w1"].shape[1], w["w2"].shape[1]
+        f = {"hq": np.zeros((P, I), np.uint8), "hs": np.zeros((P, I // 128), np.uint8),
+             "h": np.zeros((P, I), np.float32), "o": np.zeros((P, H), np.float64)}
+        used = [e for e in range(r["expert_offsets"].size - 1)
+                if r["expert_offsets"][e + 1] > r["expert_offsets"][e]]
+        # one BLAS thread per worker: the workers already fill the cores
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda es: expert_ffn(xq, xs, r, w, top_k, limit, experts=es,
+                                              weight_format=weight_format, out=f),
+                        [used[i::workers] for i in range(workers)]))
     ysh = None
     if inp.get("shared_w1") is not None:
         ysh = shared_expert(x, inp["shared_w1"], inp["shared_w3"], inp["shared_w2"], limit)

@@ -2,14 +2,18 @@
 against eager moe_layer calls: every replay must give bit-identical outputs
 and routing ("DeepSeek-V4-Flash-SI" card, 模型效果 / 质量标准: graph decoding
 identical to eager).  Replays are interleaved with eager work on the same
-device and with in-place updates of x, and each replay is checked."""
+device and with in-place updates of x, and each replay is checked; the first
+replay is also compared with the oracle."""
+
+import os
 
 import numpy as np
 import pytest
 import torch
 
 import synth
-from gpu_util import config, device_inputs
+from gpu_util import config, device_inputs, host, near_tie_tokens, norm_err
+from oracle import ffn, formats, route as oroute
 
 pytestmark = pytest.mark.gpu
 
@@ -65,5 +69,22 @@ def test_graph_replays_match_eager(name, tokens, over):
             assert torch.equal(yg.view(torch.int16), want_y.view(torch.int16)), f"replay {it}: y differs"
             for k in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_pos"):
                 assert torch.equal(g_routing[k], want_r[k]), f"replay {it}: {k} differs"
+            if it == 0:
+                yg0, rg0 = host(yg), {k: host(v) for k, v in g_routing.items()}
     finally:
         g.close()
+    # the first replay against the oracle itself, not only against eager
+    ref = ffn.layer(inp, wl.top_k, wl.route_scale, wl.swiglu_limit, wl.mode, wl.seed,
+                    workers=min(16, len(os.sched_getaffinity(0))))
+    T = inp["x"].shape[0]
+    gidx = rg0["topk_idx"].reshape(T, -1)
+    if wl.mode == "hash":
+        assert np.array_equal(gidx, ref["topk_idx"])
+        keep = np.ones(T, bool)
+    else:
+        tie = near_tie_tokens(oroute.sqrtsoftplus(ref["logits"]), inp.get("bias"), wl.top_k)
+        keep = np.all(gidx == ref["topk_idx"], axis=1)
+        assert np.all(keep | tie)
+    err = norm_err(formats.bf16_decode(yg0[keep]), ref["y"][keep])
+    print(f"graph replay vs oracle: {err:.2e} over {keep.sum()} tokens")
+    assert err <= 2e-2

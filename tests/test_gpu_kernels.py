@@ -157,19 +157,24 @@ def _ffn_case(wl, tokens, seed_tokens=None):
 # result differs from the exact dot product by up to ~2**-14 of sum|a*b|
 # (random FP4 x FP8 operands and scales); TAU allows twice that.
 TAU = 2.0 ** -13
+# Share of h codes that may differ from the oracle's (each one still has to be
+# a rounding of a value within the accumulation bound): the GEMMs' own
+# rounding differences flip 1e-4 to 4e-4 of the codes on the workloads here.
+MAX_FLIP_FRAC = 2e-3
 
 
-def _bounds(inp, xq, xs, r, ref, wl, deq=quant.mxfp4_dequant, tau=None):
+def _bounds(inp, xq, xs, r, ref, wl, deq=quant.mxfp4_dequant, tau=None, experts=None):
     """Per element of h and o: how far the GPU may sit from the oracle given
     tau (default TAU) accumulation error in each GEMM (and h's fp32
-    rounding); deq dequantizes the expert weights."""
+    rounding); deq dequantizes the expert weights; `experts` limits the
+    bounds to those experts' rows."""
     tau = TAU if tau is None else tau
     off, sp = r["expert_offsets"], r["sorted_pairs"]
     P, I = ref["hq"].shape
     dh = np.zeros((P, I))
     absw2 = {}
     lim = wl.swiglu_limit
-    for e in range(len(off) - 1):
+    for e in (range(len(off) - 1) if experts is None else experts):
         lo, hi = int(off[e]), int(off[e + 1])
         if lo == hi:
             continue
@@ -266,7 +271,7 @@ def test_expert_ffn_parity(shape):
     torch.cuda.synchronize()
     dh, absw2 = _bounds(inp, xq, xs, r, ref, wl)
     hq, hs = host(g["hq"]), host(g["hs"])
-    _check_hq(hq, hs, ref, dh, max_flip_frac=0.02)
+    _check_hq(hq, hs, ref, dh, max_flip_frac=MAX_FLIP_FRAC)
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
 
 
@@ -293,8 +298,41 @@ def test_expert_ffn_unclamped_limit():
     torch.cuda.synchronize()
     dh, absw2 = _bounds(inp, xq, xs, r, ref, wl)
     hq, hs = host(g["hq"]), host(g["hs"])
-    _check_hq(hq, hs, ref, dh, max_flip_frac=0.02)
+    _check_hq(hq, hs, ref, dh, max_flip_frac=MAX_FLIP_FRAC)
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
+
+
+def test_expert_ffn_skewed_hot_expert():
+    # The skewed workload at full size (16384 tokens, 384 experts, Zipf(1.1)
+    # popularity): the GPU runs every expert of the oracle's routing, and
+    # every pair of the most-loaded expert (~16k pairs: ~128 m-tiles in a row
+    # through the persistent tile kernel) and of the least-loaded one is
+    # checked element by element.
+    wl = synth.WORKLOADS["skewed"]
+    print("[skewed hot expert] generating inputs", flush=True)
+    inp = synth.make_inputs(wl)
+    x = inp["x"]
+    xq, xs = quant.act_quant(formats.bf16_decode(x))
+    r = oroute.route(x, inp["w_gate"], k=wl.top_k, bias=inp["bias"], route_scale=wl.route_scale)
+    load = np.diff(r["expert_offsets"])
+    hot, cold = int(np.argmax(load)), int(np.argmin(np.where(load > 0, load, 1 << 30)))
+    print(f"[skewed hot expert] expert {hot}: {load[hot]} pairs, expert {cold}: {load[cold]} pairs",
+          flush=True)
+    cfg = config(moe, wl)
+    routing = {n: dev(r[n]) for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_pos")}
+    w = {n: dev(inp[n]) for n in ("w1", "w1_scale", "w3", "w3_scale", "w2", "w2_scale")}
+    g = moe.expert_ffn(cfg, dev(xq), dev(xs), routing, w, want_h=True)
+    torch.cuda.synchronize()
+    ref = ffn.expert_ffn(xq, xs, r, inp, wl.top_k, wl.swiglu_limit, experts=[hot, cold])
+    dh, absw2 = _bounds(inp, xq, xs, r, ref, wl, experts=[hot, cold])
+    rows = np.concatenate([np.arange(r["expert_offsets"][e], r["expert_offsets"][e + 1]) for e in (hot, cold)])
+    sub = {k: ref[k][rows] for k in ("hq", "hs", "h", "o")}
+    rows_d = dev(rows)
+    hq, hs = host(g["hq"][rows_d]), host(g["hs"][rows_d])
+    _check_hq(hq, hs, sub, dh[rows], max_flip_frac=MAX_FLIP_FRAC)
+    # rows renumbered from 0: hot expert first, then the cold one
+    rs = {"expert_offsets": np.array([0, load[hot], load[hot] + load[cold]])}
+    _check_o(host(g["out"][rows_d]).astype(np.float64), hq, hs, sub, rs, {0: absw2[hot], 1: absw2[cold]})
 
 
 @pytest.mark.parametrize("T,E,H", [(1, 40, 1024), (17, 256, 4096), (37, 33, 2048), (64, 384, 4096),

@@ -11,7 +11,7 @@ import torch
 import synth
 from gpu_util import config, dev, device_inputs, host, norm_err
 from oracle import ffn, formats, quant, route as oroute
-from test_gpu_kernels import _bounds, _check_hq, _check_o
+from test_gpu_kernels import _bounds, _check_hq, MAX_FLIP_FRAC, _check_o
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def test_nvfp4_expert_ffn_parity(shape):
     torch.cuda.synchronize()
     dh, absw2 = _bounds(inp, xq, xs, r, ref, wl, deq=quant.nvfp4_dequant)
     hq, hs = host(g["hq"]), host(g["hs"])
-    _check_hq(hq, hs, ref, dh, max_flip_frac=0.02)
+    _check_hq(hq, hs, ref, dh, max_flip_frac=MAX_FLIP_FRAC)
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
 
 
