@@ -434,11 +434,12 @@ moe_status moe_expert_ffn(const moe_config* cfg, const uint8_t* xq, const uint8_
 
 namespace {
 
-// Argument checks of moe_layer (and of its graph capture), host-side only.
-moe_status layer_check(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
-                       const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
-                       const moe_shared_weights* shared, const uint16_t* y,
-                       const moe_routing* routing_out, const void* ws, size_t ws_bytes) {
+// Argument checks of moe_layer, its graph capture and its no-allocation
+// variant (everything but the workspace), host-side only.
+moe_status layer_args_check(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                            const float* bias, const int64_t* token_ids,
+                            const moe_expert_weights* w, const moe_shared_weights* shared,
+                            const uint16_t* y, const moe_routing* routing_out) {
   moe_status s = check_cfg(cfg);
   if (s != MOE_OK) return s;
   const moe_config& c = *cfg;
@@ -459,12 +460,36 @@ moe_status layer_check(const moe_config* cfg, const uint16_t* x, const uint16_t*
       return MOE_ERR_MISALIGNED;
   }
   if (routing_out && (s = check_routing_ptrs(routing_out)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+moe_status layer_check(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                       const float* bias, const int64_t* token_ids, const moe_expert_weights* w,
+                       const moe_shared_weights* shared, const uint16_t* y,
+                       const moe_routing* routing_out, const void* ws, size_t ws_bytes) {
+  moe_status s = layer_args_check(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out);
+  if (s != MOE_OK) return s;
   const size_t need = moe_workspace_size(cfg, MOE_OP_LAYER);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (need && !ws) return MOE_ERR_NULL_ARG;
   if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
   return MOE_OK;
 }
+
+// Where moe_layer runs a shared expert that does not ride in the routing
+// launches: kProcessSide forks it onto the process's per-device side stream
+// (under its mutex), kPrivateSide onto a side stream and events the caller
+// owns (graph capture: a capture-private pair, so that no other call can
+// enqueue onto a stream that joined the capture).
+enum class SharedPlacement { kProcessSide, kPrivateSide };
+
+// The launch sequence of moe_layer (arguments already checked, device
+// checked, `ws` large enough).
+moe_status layer_enqueue(const moe_config& c, const uint16_t* x, const uint16_t* w_gate,
+                         const float* bias, const int64_t* token_ids,
+                         const moe_expert_weights* w, const moe_shared_weights* shared,
+                         uint16_t* y, const moe_routing* routing_out, void* ws,
+                         hipStream_t st, SharedPlacement placement, SideStream* private_side);
 
 }  // namespace
 
@@ -478,9 +503,20 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
                              ws_bytes);
   if (s != MOE_OK) return s;
   if ((s = check_device()) != MOE_OK) return s;
-  const moe_config& c = *cfg;
+  return layer_enqueue(*cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws,
+                       static_cast<hipStream_t>(stream), SharedPlacement::kProcessSide, nullptr);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+moe_status layer_enqueue(const moe_config& c, const uint16_t* x, const uint16_t* w_gate,
+                         const float* bias, const int64_t* token_ids,
+                         const moe_expert_weights* w, const moe_shared_weights* shared,
+                         uint16_t* y, const moe_routing* routing_out, void* ws,
+                         hipStream_t st, SharedPlacement placement, SideStream* private_side) {
+  moe_status s = MOE_OK;
   Carver cv(ws);
   LayerWs l = carve_layer(cv, c);
   const moe_routing& r = routing_out ? *routing_out : l.routing;
@@ -519,9 +555,13 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   std::unique_lock<std::mutex> lock;
   SideStream* side = nullptr;
   auto fork_shared = [&]() -> moe_status {
-    if ((s = side_stream(side)) != MOE_OK) return s;
-    lock = std::unique_lock<std::mutex>(side->mu);
-    if ((s = side_init_locked(*side)) != MOE_OK) return s;
+    if (placement == SharedPlacement::kPrivateSide) {
+      side = private_side;
+    } else {
+      if ((s = side_stream(side)) != MOE_OK) return s;
+      lock = std::unique_lock<std::mutex>(side->mu);
+      if ((s = side_init_locked(*side)) != MOE_OK) return s;
+    }
     hipStream_t ss = side->stream;
     MOE_TRY(hipEventRecord(side->fork, st));
     MOE_TRY(hipStreamWaitEvent(ss, side->fork, 0));
@@ -562,6 +602,10 @@ moe_status moe_layer(const moe_config* cfg, const uint16_t* x, const uint16_t* w
   return MOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 moe_status moe_expert_cast_fp8(const moe_config* cfg, const moe_expert_weights* src,
                                const moe_expert_weights* dst, void* stream) {
   moe_status s = check_cfg(cfg);
@@ -596,20 +640,33 @@ moe_status moe_layer_graph_create(const moe_config* cfg, const uint16_t* x,
                              ws_bytes);
   if (s != MOE_OK) return s;
   if ((s = check_device()) != MOE_OK) return s;
+  // the capture stream and, for a shared expert on a side stream, a side
+  // stream and two events of this capture's own: a stream that joined the
+  // capture stays in it until hipStreamEndCapture, so no other call may
+  // enqueue onto it meanwhile
   hipStream_t cs = nullptr;
-  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
-  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
-    (void)hipStreamDestroy(cs);
+  SideStream priv;
+  auto release = [&]() {
+    if (priv.join) (void)hipEventDestroy(priv.join);
+    if (priv.fork) (void)hipEventDestroy(priv.fork);
+    if (priv.stream) (void)hipStreamDestroy(priv.stream);
+    if (cs) (void)hipStreamDestroy(cs);
+  };
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess ||
+      (shared && side_init_locked(priv) != MOE_OK) ||
+      hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    release();
     return MOE_ERR_HIP;
   }
-  s = moe_layer(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws, ws_bytes, cs);
+  s = layer_enqueue(*cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws, cs,
+                    SharedPlacement::kPrivateSide, &priv);
   hipGraph_t g = nullptr;
   const hipError_t ec = hipStreamEndCapture(cs, &g);
   if (s == MOE_OK && (ec != hipSuccess || !g)) s = MOE_ERR_HIP;
   hipGraphExec_t ge = nullptr;
   if (s == MOE_OK && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) s = MOE_ERR_HIP;
   if (g) (void)hipGraphDestroy(g);
-  (void)hipStreamDestroy(cs);
+  release();
   if (s != MOE_OK) return s;
   moe_graph* h = new (std::nothrow) moe_graph{ge};
   if (!h) {
@@ -633,3 +690,4 @@ moe_status moe_graph_destroy(moe_graph* graph) {
 }
 
 }  // extern "C"
+

@@ -48,8 +48,19 @@
  *
  * Conventions of every entry point:
  *  - All tensor pointers are DEVICE pointers to caller-owned, contiguous,
- *    row-major memory, 16-byte aligned. The library allocates nothing, keeps
- *    no state between calls and never copies data to the host.
+ *    row-major memory, 16-byte aligned. The library allocates no device
+ *    memory for a call (scratch comes from the caller's workspace), keeps no
+ *    data between calls and never copies data to the host.
+ *  - Process-level resources the library keeps (created on first use, held
+ *    until the process ends, never freed by a call): per device, a cached
+ *    architecture check and the CU count; for moe_layer calls that run the
+ *    shared expert on a second stream (see moe_layer), one side stream
+ *    (default priority, non-blocking), two events (timing disabled) and a
+ *    mutex that keeps concurrent calls' fork/join pairs from interleaving.
+ *    moe_layer_graph_create makes a capture stream and, with a shared
+ *    expert, a side stream and two events of its own, and destroys them
+ *    before it returns; the graph it returns holds its instantiated graph
+ *    until moe_graph_destroy.
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call
  *    validates its arguments on the host, enqueues its kernels on `stream`
  *    and returns; nothing is synchronised. Results are ready when the stream
@@ -201,7 +212,11 @@ moe_status moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* w
                      void* stream);
 
 /* Routed experts on pre-quantized activations (w1|w3 -> clamped SwiGLU ->
- * FP8 requant -> w2), in sorted-pair order.
+ * FP8 requant -> w2), in sorted-pair order ("DeepSeek-V4-Flash-SI" card,
+ * 架构特性: the MoE paragraph's SwiGLU with its activation clamped to
+ * +-limit for every selected expert; the 低精度计算 paragraph's FP4 E2M1
+ * weights with an E8M0 scale per 32 and online FP8 E4M3 activations with a
+ * power-of-two scale per 128 -- here both expert inputs, x and h).
  *   xq [T, H] E4M3, xs [T, H/128] E8M0 (from moe_quant_act)
  *   r: expert_offsets and sorted_pairs are read (topk_* and pair_pos unused)
  *   out_pairs [P, H]: fp32 if cfg->out_fp32 else bf16; row i belongs to
@@ -214,8 +229,16 @@ moe_status moe_expert_ffn(const moe_config* cfg, const uint8_t* xq, const uint8_
                           uint8_t* hq_out, uint8_t* hs_out, void* ws, size_t ws_bytes,
                           void* stream);
 
-/* The whole layer: route, quantize x, routed experts, shared expert (if
- * `shared` is non-NULL), weighted combine.
+/* The whole layer ("DeepSeek-V4-Flash-SI" card, 架构特性: the MoE
+ * paragraph's per-token top-k routed experts -- sqrtsoftplus scores, or hash
+ * routing from the token id -- with routing scale 1.5, plus one shared
+ * expert, every expert a SwiGLU clamped to +-limit; the 低精度计算
+ * paragraph's FP4 expert weights, online FP8 activations and bf16 gate and
+ * shared expert): route, quantize x, routed experts, shared expert (if
+ * `shared` is non-NULL), weighted combine.  A shared expert that does not
+ * ride in the decode-sized routing launches runs on this library's side
+ * stream for the device, forked from `stream` and joined back before the
+ * combine (see the conventions above).
  *   x [T, H] bf16; w_gate [E, H] bf16 (score mode); bias [E] fp32 or NULL;
  *   token_ids [T] int64 (hash mode); y [T, H] bf16 (out).
  *   routing_out: NULL, or arrays that receive the routing (all required).

@@ -192,3 +192,4 @@ def test_expert_ffn_argument_errors():
     assert lib.moe_expert_ffn(ctypes.byref(c), 16, 24, ctypes.byref(r), ctypes.byref(w), 16, None, None, 16, big, None) == 3
     need = lib.moe_workspace_size(ctypes.byref(c), moe.OP_EXPERT_FFN)
     assert lib.moe_expert_ffn(ctypes.byref(c), 16, 16, ctypes.byref(r), ctypes.byref(w), 16, None, None, 16, need - 1, None) == 4
+
