@@ -4,10 +4,13 @@
 
 One step = one call of moe_layer (route, quantize, routed experts, shared
 expert, combine) over one batch of seeded synthetic input already resident in
-HBM.  Prints ONE JSON line: whole-layer tokens/s, the roofline of the routed
-expert FFN (grouped GEMM1 + fused SwiGLU/requant + GEMM2, timed with HIP
-events on the stream it runs on), and the CPU oracle timed on a bounded token
-sample of the same workload on this host's cores.
+HBM.  Prints ONE JSON line: whole-layer tokens/s of the decode batch (64
+tokens), the roofline of its routed expert FFN (grouped GEMM1 + fused
+SwiGLU/requant + GEMM2, timed with HIP events on the stream it runs on), the
+prefill half of the metric (the same layer on 4096 tokens: tokens/s, routed
+FFN TFLOP/s against the scaled-MFMA peak and its weight stream against HBM),
+and the CPU oracle timed on a bounded token sample of the decode workload on
+this host's cores.
 """
 
 import argparse
@@ -43,6 +46,9 @@ def parse():
                          "as INT4 with synthetic float32 scales per 128)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 4096-token prefill measurement that the decode line carries")
+    ap.add_argument("--prefill-steps", type=int, default=30)
     return ap.parse_args()
 
 
@@ -51,12 +57,15 @@ def algorithmic(wl, n_touched, fmt="mxfp4"):
     intermediates): weights of the touched experts (FP4 nibbles + E8M0
     scales per 32 of w1, w3, w2; FP8 experts: E4M3 bytes + E8M0 per 128;
     NVFP4: nibbles + E4M3 per 16; W4AFP8: INT4 nibbles + float32 per 128),
-    the bf16 shared expert and gate, x in, y out."""
+    the bf16 shared expert and gate, x in, y out.  The routed expert FFN's
+    share is the touched experts' weights: its FP8 activations, h and the
+    per-pair outputs are intermediates of the layer, overhead rather than
+    work."""
     T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.n_experts, wl.top_k
     per_expert = {"mxfp4": 3 * (I * H // 2 + I * H // 32), "fp8": 3 * (I * H + I * H // 128),
                   "nvfp4": 3 * (I * H // 2 + I * H // 16),
                   "w4afp8": 3 * (I * H // 2 + 4 * (I * H // 128))}[fmt]
-    ffn_bytes = n_touched * per_expert + T * (H + H // 128) + T * k * H * 4
+    ffn_bytes = n_touched * per_expert
     shared = 3 * I * H * 2 if wl.shared else 0
     gate = E * H * 2 if wl.mode != "hash" else 0
     layer_bytes = n_touched * per_expert + shared + gate + 2 * T * H * 2
@@ -106,17 +115,25 @@ def cpu_baseline(wl, inp, budget_s=20.0, weight_format="mxfp4"):
         t_used += dt
         if dt < budget_s / 4:
             n *= 2
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": done / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{done} tokens of the {wl.name} workload (T={wl.tokens}), whole layer incl. "
                       f"routing and dequantization, {t_used:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU expert-parallel path is a design, not code)"}))
-        sys.exit(2)
+def measure(args, wl, steps, with_graph=True, with_cpu=False):
+    """Times the layer (eager calls, and replays of the same call captured
+    into a HIP graph) and the routed expert FFN alone on workload `wl`.
+    Returns a dict of figures; the caller frees the inputs with it."""
+    import ctypes
 
     import numpy as np
     import torch
@@ -124,9 +141,6 @@ def main():
     import block_scaled_fp4_sqrtsoftplus_amd as moe
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    steps = args.steps or {"tiny": 200, "decode": 100, "prefill": 30, "skewed": 10, "hash": 10}[wl.name]
-    torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     t0 = time.time()
     inp = synth.make_inputs(wl)
@@ -148,8 +162,7 @@ def main():
                      top_k=wl.top_k, route_scale=wl.route_scale, swiglu_limit=wl.swiglu_limit,
                      route_mode=moe.ROUTE_HASH if wl.mode == "hash" else moe.ROUTE_SQRTSOFTPLUS,
                      hash_seed=wl.seed)
-    fp8 = args.experts == "fp8"
-    if fp8:
+    if args.experts == "fp8":
         w = moe.expert_cast_fp8(cfg, w)
         cfg.expert_format = moe.EXPERTS_FP8
         torch.cuda.synchronize()
@@ -166,38 +179,40 @@ def main():
     L = moe.Layer(cfg, w, w_gate=wg, bias=bias, shared=shared)
     y = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device=dev)
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
-    print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {wl}", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: inputs ready in {time.time() - t0:.1f}s: {wl}", file=sys.stderr,
+          flush=True)
 
-    # ---- whole layer: eager calls (the step that sets `value`), then replays
-    # of the same call captured into a HIP graph (sets `value` with --graph) ----
-    def timed(step_fn):
+    def timed(step_fn, n):
         for _ in range(args.warmup):
             step_fn()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_start = time.perf_counter()
         ev0.record()
-        for _ in range(steps):
+        for _ in range(n):
             step_fn()
         ev1.record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t_start) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+        return (time.perf_counter() - t_start) * 1e3 / n, ev0.elapsed_time(ev1) / n
 
-    eager_ms, eager_gpu_ms = timed(lambda: L(x, ids, y=y, routing=routing))
-    graph = moe.LayerGraph(L, x, token_ids=ids, y=y, routing=routing)
-    graph_ms, graph_gpu_ms = timed(graph.launch)
-    graph.close()
-    launch = "graph" if args.graph else "eager"
-    ms_step, gpu_ms_step = (graph_ms, graph_gpu_ms) if args.graph else (eager_ms, eager_gpu_ms)
-    n_touched = int(np.sum(np.diff(routing["expert_offsets"].cpu().numpy()) > 0))
+    # whole layer: eager calls (the step), then replays of the same call
+    # captured into a HIP graph
+    eager_ms, eager_gpu_ms = timed(lambda: L(x, ids, y=y, routing=routing), steps)
+    graph_ms = graph_gpu_ms = None
+    if with_graph:
+        graph = moe.LayerGraph(L, x, token_ids=ids, y=y, routing=routing)
+        graph_ms, graph_gpu_ms = timed(graph.launch, steps)
+        graph.close()
     load = np.diff(routing["expert_offsets"].cpu().numpy())
+    n_touched = int(np.sum(load > 0))
 
-    # ---- routed expert FFN (the dominant work) on the same routing ----
+    # routed expert FFN (grouped GEMM1 + fused SwiGLU/requant + GEMM2) on the
+    # same routing, timed with events on the stream it is launched on (the
+    # current stream: torch's events record there)
     xq, xs = moe.quant_act(x)
     ffn_out = torch.empty((wl.tokens * wl.top_k, wl.hidden), dtype=torch.float32, device=dev)
     ws_n = moe.workspace_size(cfg, moe.OP_EXPERT_FFN)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-    import ctypes
     cc, rc, wc = cfg.c(), moe._routing_c(routing), moe._weights_c(w)
 
     def ffn_call():
@@ -207,61 +222,127 @@ def main():
         if st != 0:
             raise moe.MoeError(st)
 
-    for _ in range(args.warmup):
-        ffn_call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        ffn_call()
-    e1.record()
-    torch.cuda.synchronize()
-    ffn_ms = e0.elapsed_time(e1) / steps
+    _, ffn_ms = timed(ffn_call, steps)
 
     alg = algorithmic(wl, n_touched, args.experts)
+    # the NVFP4 path dequantizes to fp16 and runs on the fp16 MFMA (the bf16 / fp16 peak)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if args.experts == "nvfp4" else MFMA_FP8_PEAK_TFLOPS
+    ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
+    ffn_tflops = alg["flops_routed"] / (ffn_ms * 1e-3) / 1e12
+    layer_t_roof = max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
+                       alg["flops_routed"] / (mfma_peak * 1e12)
+                       + alg["flops_shared"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                       + alg["flops_router"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    cpu = None
+    if with_cpu:
+        cpu = cpu_baseline(wl, inp, weight_format=args.experts)   # inp holds the NVFP4 / W4AFP8 scales then
     src_name = {"nvfp4": "expert_gemm_nv.hip", "w4afp8": "expert_gemm_w4.hip"}.get(args.experts, "expert_gemm.hip")
     src = open(os.path.join(ROOT, "block_scaled_fp4_sqrtsoftplus_amd", "csrc", src_name), "rb").read()
     traffic = traffic_record(hashlib.sha256(src).hexdigest(),
                              wl.name + ("" if args.experts == "mxfp4" else "_" + args.experts))
-    ffn_gbs = alg["ffn_bytes"] / (ffn_ms * 1e-3) / 1e9
-    ffn_tflops = alg["flops_routed"] / (ffn_ms * 1e-3) / 1e12
-    # the NVFP4 path dequantizes to fp16 and runs on the fp16 MFMA (the bf16 / fp16 peak)
-    mfma_peak = MFMA_BF16_PEAK_TFLOPS if args.experts == "nvfp4" else MFMA_FP8_PEAK_TFLOPS
-    hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (mfma_peak * 1e12)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(ffn_tflops / mfma_peak, 4), "traffic": traffic}
     small = wl.tokens * wl.top_k <= 32 * wl.n_experts
-    fam = {"fp8": "expert_gemm_stream8" if small else "expert_gemm_kernel",
+    fam = {"fp8": "expert_gemm_stream8" if small else "expert_gemm_tile",
            "nvfp4": "expert_gemm_nv", "w4afp8": "expert_gemm_w4",
            "mxfp4": "expert_gemm_stream" if small else "expert_gemm_tile"}[args.experts]
     if args.experts in ("nvfp4", "w4afp8"):
-        roof["kernel"] = f"routed expert FFN: {fam}<1> + {fam}<2> (+ tile prefix)"
+        kname = f"{fam}<1> + {fam}<2>"
+    elif args.experts == "fp8" and not small:
+        kname = f"{fam}<1,{wl.hidden // 128},true> + {fam}<2,{wl.inter // 128},true>"
     else:
-        roof["kernel"] = (f"routed expert FFN: {fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
-                          " (+ tile prefix)")
-    roof["ms_per_call"] = round(ffn_ms, 4)
+        kname = f"{fam}<1,{wl.hidden // 128}> + {fam}<2,{wl.inter // 128}>"
+    return {
+        "wl": wl, "eager_ms": eager_ms, "eager_gpu_ms": eager_gpu_ms, "graph_ms": graph_ms,
+        "graph_gpu_ms": graph_gpu_ms, "n_touched": n_touched,
+        "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2),
+        "alg": alg, "ffn_ms": ffn_ms, "ffn_gbs": ffn_gbs, "ffn_tflops": ffn_tflops,
+        "mfma_peak": mfma_peak, "layer_t_roof": layer_t_roof, "cpu": cpu, "traffic": traffic,
+        "kernel": f"routed expert FFN: {kname} (+ tile prefix)",
+    }
+
+
+def workload_summary(m, launch="eager"):
+    """Both roofline fractions of a measured workload: the layer against
+    max(bytes / HBM, sum of flops / MFMA peaks), and the routed expert FFN
+    against HBM (its weight stream) and against the scaled-MFMA peak."""
+    wl = m["wl"]
+    ms = m["graph_ms"] if launch == "graph" else m["eager_ms"]
+    return {
+        "workload": f"T={wl.tokens} H={wl.hidden} I={wl.inter} E={wl.n_experts} top-{wl.top_k}",
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+        "layer_roofline_frac": round(m["layer_t_roof"] / (ms * 1e-3), 4),
+        "routed_ffn_ms": round(m["ffn_ms"], 4),
+        "routed_ffn_tflops": round(m["ffn_tflops"], 1),
+        "routed_ffn_mfma_frac": round(m["ffn_tflops"] / m["mfma_peak"], 4),
+        "routed_ffn_weight_gbs": round(m["ffn_gbs"], 1),
+        "routed_ffn_hbm_frac": round(m["ffn_gbs"] / HBM_PEAK_GBS, 4),
+        "experts_touched": m["n_touched"],
+        "max_over_mean_load": m["max_over_mean_load"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU expert-parallel path is a design, not code)"}))
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    steps = args.steps or {"tiny": 200, "decode": 100, "prefill": 30, "skewed": 10, "hash": 10}[wl.name]
+    m = measure(args, wl, steps, with_graph=True, with_cpu=not args.no_cpu_baseline)
+    launch = "graph" if args.graph else "eager"
+    ms_step = m["graph_ms"] if args.graph else m["eager_ms"]
+    gpu_ms_step = m["graph_gpu_ms"] if args.graph else m["eager_gpu_ms"]
+    alg = m["alg"]
+
+    hbm_bound = alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops_routed"] / (m["mfma_peak"] * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(m["ffn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(m["ffn_gbs"] / HBM_PEAK_GBS, 4), "traffic": m["traffic"]}
+    else:
+        roof = {"bound": "mfma", "achieved": round(m["ffn_tflops"], 1), "peak": m["mfma_peak"],
+                "unit": "TFLOP/s", "frac": round(m["ffn_tflops"] / m["mfma_peak"], 4),
+                "traffic": m["traffic"]}
+    roof["kernel"] = m["kernel"]
+    roof["ms_per_call"] = round(m["ffn_ms"], 4)
     roof["alg_bytes_per_call"] = alg["ffn_bytes"]
     roof["alg_flops_per_call"] = alg["flops_routed"]
+    layer = workload_summary(m, launch)
+    layer.update({"launch": launch, "gpu_ms_per_step": round(gpu_ms_step, 4),
+                  "eager_ms_per_step": round(m["eager_ms"], 4),
+                  "graph_ms_per_step": round(m["graph_ms"], 4), "alg_bytes": alg["layer_bytes"],
+                  "hbm_gbs": round(alg["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1)})
+    cpu = m["cpu"]
+    del m
+    torch.cuda.empty_cache()
 
-    layer_t_roof = max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
-                       alg["flops_routed"] / (mfma_peak * 1e12)
-                       + alg["flops_shared"] / 2.5e15 + alg["flops_router"] / 2.5e15)
+    # the prefill half of the metric: the same layer on a 4096-token batch
+    prefill = None
+    if wl.name == "decode" and not args.no_prefill:
+        mp = measure(args, synth.WORKLOADS["prefill"], args.prefill_steps, with_graph=False)
+        prefill = workload_summary(mp)
+        prefill["kernel"] = mp["kernel"]
+        prefill["traffic"] = mp["traffic"]
+        del mp
+        torch.cuda.empty_cache()
+
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        dev = torch.device("cuda:0")
         src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst_buf = torch.empty_like(src_buf)
         for _ in range(3):
             dst_buf.copy_(src_buf)
         torch.cuda.synchronize()
         del src_buf, dst_buf
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, weight_format=args.experts)   # inp holds the NVFP4 / W4AFP8 scales then
 
+    fp8 = args.experts == "fp8"
     value = wl.tokens / (ms_step * 1e-3)
     out = {
         "metric": "MoE layer tokens/s + % roofline (HBM GB/s decode, scaled-MFMA TFLOPS prefill)",
@@ -285,16 +366,11 @@ def main():
                                f"{', FP8 experts (per-128 cast of the MXFP4 weights)' if fp8 else ''}"
                                f"{', NVFP4 experts (per-16 E4M3 scales)' if args.experts == 'nvfp4' else ''}"
                                f"{', W4AFP8 experts (INT4, f32 scale per 128)' if args.experts == 'w4afp8' else ''}",
-                   "tokens": wl.tokens, "experts_touched": n_touched,
-                   "max_over_mean_load": round(float(load.max() / max(load.mean(), 1e-9)), 2)},
-        "layer": {"launch": launch,
-                  "gpu_ms_per_step": round(gpu_ms_step, 4),
-                  "eager_ms_per_step": round(eager_ms, 4),
-                  "graph_ms_per_step": round(graph_ms, 4),
-                  "alg_bytes": alg["layer_bytes"],
-                  "hbm_gbs": round(alg["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1),
-                  "roofline_frac": round(layer_t_roof / (ms_step * 1e-3), 4)},
+                   "tokens": wl.tokens, "experts_touched": layer["experts_touched"],
+                   "max_over_mean_load": layer["max_over_mean_load"]},
+        "layer": layer,
         "roofline": roof,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
