@@ -28,7 +28,8 @@ lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK = 0
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL_ARG", "MOE_ERR_BAD_SHAPE", "MOE_ERR_MISALIGNED",
-                "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_UNSUPPORTED", "MOE_ERR_ARCH", "MOE_ERR_HIP"]
+                "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_UNSUPPORTED", "MOE_ERR_ARCH", "MOE_ERR_HIP",
+                "MOE_ERR_SCRATCH_TOO_SMALL"]
 ROUTE_SQRTSOFTPLUS, ROUTE_HASH = 0, 1
 EXPERTS_MXFP4, EXPERTS_FP8, EXPERTS_NVFP4, EXPERTS_W4AFP8 = 0, 1, 2, 3
 OP_ROUTE, OP_EXPERT_FFN, OP_LAYER = 0, 1, 2
@@ -85,6 +86,11 @@ lib.moe_graph_launch.restype = ctypes.c_int
 lib.moe_graph_launch.argtypes = [_vp, _vp]
 lib.moe_graph_destroy.restype = ctypes.c_int
 lib.moe_graph_destroy.argtypes = [_vp]
+lib.moe_layer_noalloc.restype = ctypes.c_int
+lib.moe_layer_noalloc.argtypes = [ctypes.POINTER(MoeConfigC), _vp, _vp, _vp, _vp,
+                                  ctypes.POINTER(MoeExpertWeightsC), ctypes.POINTER(MoeSharedWeightsC),
+                                  _vp, ctypes.POINTER(MoeRoutingC), _vp]
+NOALLOC_SCRATCH_BYTES = 64 << 20    # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -292,6 +298,21 @@ class LayerGraph:
             self.close()
         except Exception:
             pass
+
+
+def layer_noalloc(cfg: Config, x, weights, y, w_gate=None, bias=None, token_ids=None, shared=None,
+                  routing=None):
+    """moe_layer_noalloc: the whole layer on the library's static device
+    scratch (no workspace, nothing allocated by the call); y [T, H] bf16 and
+    the optional routing arrays are the caller's."""
+    c = cfg.c()
+    wc = _weights_c(weights)
+    sc = MoeSharedWeightsC(*(_ptr(shared[n]) for n in ("w1", "w3", "w2"))) if shared else None
+    rc = _routing_c(routing) if routing is not None else None
+    _check(lib.moe_layer_noalloc(ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(token_ids),
+                                 ctypes.byref(wc), ctypes.byref(sc) if sc is not None else None,
+                                 _ptr(y), ctypes.byref(rc) if rc is not None else None, _stream()))
+    return y
 
 
 def layer(cfg: Config, x, weights, w_gate=None, bias=None, token_ids=None, shared=None,

@@ -344,6 +344,9 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: combination not implemented";
     case MOE_ERR_ARCH: return "MOE_ERR_ARCH: the current device is not gfx950 (MI355X)";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call or kernel launch failed";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "MOE_ERR_SCRATCH_TOO_SMALL: the call needs more workspace than the static scratch "
+             "of moe_layer_noalloc holds (MOE_NOALLOC_SCRATCH_BYTES); use moe_layer";
   }
   return "MOE_ERR_UNKNOWN";
 }
@@ -480,8 +483,9 @@ moe_status layer_check(const moe_config* cfg, const uint16_t* x, const uint16_t*
 // launches: kProcessSide forks it onto the process's per-device side stream
 // (under its mutex), kPrivateSide onto a side stream and events the caller
 // owns (graph capture: a capture-private pair, so that no other call can
-// enqueue onto a stream that joined the capture).
-enum class SharedPlacement { kProcessSide, kPrivateSide };
+// enqueue onto a stream that joined the capture), kInline on the caller's
+// stream after routing (no stream or event is created).
+enum class SharedPlacement { kProcessSide, kPrivateSide, kInline };
 
 // The launch sequence of moe_layer (arguments already checked, device
 // checked, `ws` large enough).
@@ -555,6 +559,15 @@ moe_status layer_enqueue(const moe_config& c, const uint16_t* x, const uint16_t*
   std::unique_lock<std::mutex> lock;
   SideStream* side = nullptr;
   auto fork_shared = [&]() -> moe_status {
+    if (placement == SharedPlacement::kInline) {
+      // no side stream: the shared expert's GEMMs run here, in stream order
+      MOE_TRY(launch_shared_up(x, shared->w1, shared->w3, l.hsh, l.shpart, c.tokens, c.hidden,
+                               c.inter, c.swiglu_limit, st));
+      MOE_TRY(launch_shared_down(l.hsh, shared->w2, l.ysh, l.shpart, c.tokens, c.hidden,
+                                 c.inter, st));
+      ysh = l.ysh;
+      return MOE_OK;
+    }
     if (placement == SharedPlacement::kPrivateSide) {
       side = private_side;
     } else {
@@ -574,7 +587,8 @@ moe_status layer_enqueue(const moe_config& c, const uint16_t* x, const uint16_t*
     return MOE_OK;
   };
   const bool side_shared = shared && !fused_shared;
-  const bool early_fork = side_shared && c.tokens >= kEarlyForkTokens;
+  const bool early_fork = side_shared && c.tokens >= kEarlyForkTokens &&
+                          placement != SharedPlacement::kInline;
   // score routing forks right after the router GEMM is enqueued, hash routing
   // before the quantization
   const bool fork_after_router = early_fork && c.route_mode == MOE_ROUTE_SQRTSOFTPLUS;
@@ -592,7 +606,8 @@ moe_status layer_enqueue(const moe_config& c, const uint16_t* x, const uint16_t*
   if ((s = enqueue_ffn(c, l.xq, l.xs, r, *w, l.o, 1, l.ffn.hq, l.ffn.hs, l.ffn.mtile_off, st,
                        tiles_done)) != MOE_OK)
     return s;
-  if (side_shared) MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
+  if (side_shared && placement != SharedPlacement::kInline)
+    MOE_TRY(hipStreamWaitEvent(st, side->join, 0));
   if (fused_shared) {
     ysh = l.shpart;
     ysh_parts = c.inter / kSharedSplitK;
@@ -691,3 +706,53 @@ moe_status moe_graph_destroy(moe_graph* graph) {
 
 }  // extern "C"
 
+// Workspace of moe_layer_noalloc: a device array of MOE_NOALLOC_SCRATCH_BYTES
+// in this library's code object, one copy per device, alive until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host the
+// name is only a registration handle); it takes the device address from
+// hipGetSymbolAddress once per device and uses that.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[64];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  ScratchAddr& a = g_scratch[dev];
+  std::call_once(a.once, [&a]() {
+    a.err = hipGetSymbolAddress(&a.ptr, HIP_SYMBOL(scratch));
+  });
+  if (a.err != hipSuccess || !a.ptr) return MOE_ERR_HIP;
+  *out = a.ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_noalloc(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                             const float* bias, const int64_t* token_ids,
+                             const moe_expert_weights* w, const moe_shared_weights* shared,
+                             uint16_t* y, const moe_routing* routing_out, void* stream) {
+  moe_status s = layer_args_check(cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out);
+  if (s != MOE_OK) return s;
+  if (moe_workspace_size(cfg, MOE_OP_LAYER) > MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_SCRATCH_TOO_SMALL;
+  if ((s = check_device()) != MOE_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != MOE_OK) return s;
+  return layer_enqueue(*cfg, x, w_gate, bias, token_ids, w, shared, y, routing_out, ws,
+                       static_cast<hipStream_t>(stream), SharedPlacement::kInline, nullptr);
+}
+
+}  // extern "C"

@@ -56,7 +56,8 @@
  *    architecture check and the CU count; for moe_layer calls that run the
  *    shared expert on a second stream (see moe_layer), one side stream
  *    (default priority, non-blocking), two events (timing disabled) and a
- *    mutex that keeps concurrent calls' fork/join pairs from interleaving.
+ *    mutex that keeps concurrent calls' fork/join pairs from interleaving;
+ *    for moe_layer_noalloc, its static device scratch.
  *    moe_layer_graph_create makes a capture stream and, with a shared
  *    expert, a side stream and two events of its own, and destroys them
  *    before it returns; the graph it returns holds its instantiated graph
@@ -89,7 +90,9 @@ typedef enum moe_status {
   MOE_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < moe_workspace_size(...)      */
   MOE_ERR_UNSUPPORTED = 5,         /* a valid but unimplemented combination   */
   MOE_ERR_ARCH = 6,                /* the current device is not gfx950        */
-  MOE_ERR_HIP = 7                  /* a HIP launch reported an error          */
+  MOE_ERR_HIP = 7,                 /* a HIP launch reported an error          */
+  MOE_ERR_SCRATCH_TOO_SMALL = 8    /* moe_layer_noalloc: the call needs more
+                                      than MOE_NOALLOC_SCRATCH_BYTES        */
 } moe_status;
 
 typedef enum moe_route_mode {
@@ -280,6 +283,29 @@ moe_status moe_layer_graph_create(const moe_config* cfg, const uint16_t* x,
                                   moe_graph** graph_out);
 moe_status moe_graph_launch(const moe_graph* graph, void* stream);
 moe_status moe_graph_destroy(moe_graph* graph);   /* NULL is a no-op */
+
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It runs the same kernels as moe_layer on a
+ * static device scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends; it calls no
+ * allocation routine and creates no stream or event (a shared expert that
+ * moe_layer would fork onto its side stream runs on `stream` in order).
+ * Arguments and results are those of moe_layer.
+ * Errors: those of moe_layer's argument checks, reported before any GPU
+ * call; MOE_ERR_SCRATCH_TOO_SMALL when moe_workspace_size(cfg,
+ * MOE_OP_LAYER) exceeds the scratch (then nothing is enqueued; moe_layer
+ * with a caller workspace handles the call).  64 MiB hold, e.g., the layer
+ * at hidden 4096, inter 2048, 256 experts, top-6 up to 256 tokens.
+ * Every call on a device shares that device's scratch and leaves its
+ * contents behind (no kernel needs it cleared): calls that may overlap on
+ * one device -- on different streams, or from different threads without
+ * ordering -- race on it and must not be issued. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_noalloc(const moe_config* cfg, const uint16_t* x, const uint16_t* w_gate,
+                             const float* bias, const int64_t* token_ids,
+                             const moe_expert_weights* w, const moe_shared_weights* shared,
+                             uint16_t* y, const moe_routing* routing_out, void* stream);
 
 #ifdef __cplusplus
 }

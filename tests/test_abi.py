@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_quant_act", "moe_route",
                           "moe_expert_ffn", "moe_layer", "moe_layer_graph_create",
-                          "moe_graph_launch", "moe_graph_destroy", "moe_expert_cast_fp8"}
+                          "moe_graph_launch", "moe_graph_destroy", "moe_expert_cast_fp8",
+                          "moe_layer_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -193,3 +194,23 @@ def test_expert_ffn_argument_errors():
     need = lib.moe_workspace_size(ctypes.byref(c), moe.OP_EXPERT_FFN)
     assert lib.moe_expert_ffn(ctypes.byref(c), 16, 16, ctypes.byref(r), ctypes.byref(w), 16, None, None, 16, need - 1, None) == 4
 
+
+def test_noalloc_rejects_beyond_scratch():
+    # moe_layer_noalloc refuses a call whose workspace exceeds its static
+    # scratch before any HIP call (4096 tokens of the V4-Flash layer need
+    # ~0.5 GB), and checks its arguments like moe_layer
+    big = _cfg(tokens=4096)
+    assert lib.moe_workspace_size(ctypes.byref(big), moe.OP_LAYER) > moe.NOALLOC_SCRATCH_BYTES
+    w = moe.MoeExpertWeightsC(*([16] * 6))
+    st = lib.moe_layer_noalloc(ctypes.byref(big), 16, 16, None, None, ctypes.byref(w), None, 16,
+                               None, None)
+    assert moe.STATUS_NAMES[st] == "MOE_ERR_SCRATCH_TOO_SMALL"
+    small = _cfg(tokens=64)
+    assert lib.moe_workspace_size(ctypes.byref(small), moe.OP_LAYER) <= moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_noalloc(ctypes.byref(small), None, 16, None, None, ctypes.byref(w), None,
+                                 16, None, None) == 1          # x NULL
+    assert lib.moe_layer_noalloc(ctypes.byref(small), 8, 16, None, None, ctypes.byref(w), None,
+                                 16, None, None) == 3          # x misaligned
+    bad = _cfg(hidden=100)
+    assert lib.moe_layer_noalloc(ctypes.byref(bad), 16, 16, None, None, ctypes.byref(w), None,
+                                 16, None, None) == 2
