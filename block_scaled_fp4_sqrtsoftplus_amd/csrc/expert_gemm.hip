@@ -387,9 +387,34 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
 // 1024, 2048 or 4096: every wave keeps four K steps of weight and
 // activation loads in flight in a register ring (no register copies, no
 // branches around the loads, so the waits before each step's MFMAs cover
-// only that step), and reads each weight row's scales once.  Lanes whose pair slot lies past the expert's last pair read that
-// last pair's row: their columns are computed and dropped.
+// only that step), and reads each weight row's scales once.  Weights go
+// out as whole 128-byte lines (two K steps of 8 rows per load, non-
+// temporal) and two cross-lane moves per register pair turn a tile's two
+// line loads into its two steps' MFMA operands (line_pair_to_steps).  Lanes
+// whose pair slot lies past the expert's last pair read that last pair's
+// row: their columns are computed and dropped.
 // ---------------------------------------------------------------------------
+// Two line loads of a 16-row weight tile: x0 lane (g, c) holds row c % 8,
+// x1 lane (g, c) row 8 + c % 8, both at bytes 64 * (c / 8) + 16 * g of the
+// rows' 128-byte line (K steps s, s + 1).  Step s's operand needs row c,
+// bytes 16 * g in lane (g, c); step s + 1's row c, bytes 64 + 16 * g.  So
+// step s is x0's lanes 0-7 of each 16-lane row with x1's lanes 0-7 moved up
+// by 8, and step s + 1 is x1's lanes 8-15 with x0's lanes 8-15 moved down by
+// 8: one DPP row shift per dword, the bank mask picking the moved half.
+constexpr int kDppRowShr8 = 0x118, kDppRowShl8 = 0x108;
+__device__ __forceinline__ void line_pair_to_steps(uint4& x0, uint4& x1) {
+  auto lo = [](uint32_t keep, uint32_t from) {  // lanes 8-15 <- from's lanes 0-7
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShr8, 0xF, 0xC, false);
+  };
+  auto hi = [](uint32_t keep, uint32_t from) {  // lanes 0-7 <- from's lanes 8-15
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShl8, 0xF, 0x3, false);
+  };
+  const uint4 s0 = make_uint4(lo(x0.x, x1.x), lo(x0.y, x1.y), lo(x0.z, x1.z), lo(x0.w, x1.w));
+  const uint4 s1 = make_uint4(hi(x1.x, x0.x), hi(x1.y, x0.y), hi(x1.z, x0.z), hi(x1.w, x0.w));
+  x0 = s0;
+  x1 = s1;
+}
+
 template <int MODE, int S>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
   constexpr int K = S * 128;                // S in {8, 16, 32}
@@ -407,28 +432,34 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
   const size_t wrow_bytes = (size_t)K / 2;
   const size_t srow_bytes = (size_t)K / 32;
 
-  const uint8_t* wptr[4];
+  // Tile t of the wave is 16 weight rows from row0; its MFMA operand lane
+  // (grp, col) is row row0 + col.  The line loads: lane (grp, col) reads row
+  // row0 + col % 8 (first load) or row0 + 8 + col % 8 (second), bytes
+  // 64 * (col / 8) + 16 * grp of the line, so each load covers 8 whole lines.
+  const uint8_t* wtile[4];  // wave-uniform: row row0 of tile t
   const uint8_t* sptr[4];
   int n0;
   bool wave_live = true;
+  // lane offset of the first line load (the second is 8 rows further)
+  const uint32_t loff = (uint32_t)((col & 7) * wrow_bytes + 64 * (col >> 3) + 16 * grp);
   if (MODE == 1) {
     n0 = n_tile * kG1Cols;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const int row0 = n0 + 32 * wv + 16 * (t & 1);
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const uint8_t* sbase = (t < 2) ? p.w_scale : p.w3_scale;
-      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = sbase + ((size_t)e * N + row) * srow_bytes;
+      wtile[t] = base + ((size_t)e * N + row0) * wrow_bytes;
+      sptr[t] = sbase + ((size_t)e * N + row0 + col) * srow_bytes;
     }
   } else {
     n0 = n_tile * kG2Rows;
     wave_live = (n0 + 64 * wv) < N;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
-      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
-      sptr[t] = p.w_scale + ((size_t)e * N + row) * srow_bytes;
+      const int row0 = wave_live ? (n0 + 64 * wv + 16 * t) : 0;
+      wtile[t] = p.w + ((size_t)e * N + row0) * wrow_bytes;
+      sptr[t] = p.w_scale + ((size_t)e * N + row0 + col) * srow_bytes;
     }
   }
   const int slot = min(m0 + col, n_e - 1);
@@ -464,14 +495,15 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
         SR[t][0] = v.x; SR[t][1] = v.y;
       }
     }
-    // steps s and s + 1 (s even) together: the two 64-byte halves of each
-    // weight row's 128-byte line are requested back to back, so the second
-    // request meets the first one's line fill instead of missing again
+    // steps s and s + 1 (s even) together: the 128-byte line of the two
+    // steps of tile t's rows 0-7 into a0[t], of rows 8-15 into a1[t]
+    // (line_pair_to_steps makes them step s's and step s + 1's operands)
+    const size_t w8 = 8 * wrow_bytes;
     auto load_pair = [&](int s, uint4 (&a0)[4], uint4 (&b0)[2], uint4 (&a1)[4], uint4 (&b1)[2]) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        a0[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64);
-        a1[t] = *reinterpret_cast<const uint4*>(wptr[t] + (size_t)s * 64 + 64);
+        a0[t] = wload16(wtile[t] + loff + s * 64);
+        a1[t] = wload16(wtile[t] + w8 + loff + s * 64);
       }
       b0[0] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128);
       b0[1] = *reinterpret_cast<const uint4*>(bptr + (size_t)s * 128 + 64);
@@ -491,6 +523,10 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArg
       if constexpr (LOADS) sbn = load_sb(q + 1);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        if ((d & 1) == 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) line_pair_to_steps(A[d][t], A[d + 1][t]);
+        }
         // byte 4s + grp of the row's scales sits in lane group (4s)/S,
         // dword s % SD, byte grp
         const int s = 4 * q + d;
