@@ -394,27 +394,6 @@ __global__ __launch_bounds__(kGemmThreads) void expert_gemm_kernel(ExpertGemmArg
 // whose pair slot lies past the expert's last pair read that last pair's
 // row: their columns are computed and dropped.
 // ---------------------------------------------------------------------------
-// Two line loads of a 16-row weight tile: x0 lane (g, c) holds row c % 8,
-// x1 lane (g, c) row 8 + c % 8, both at bytes 64 * (c / 8) + 16 * g of the
-// rows' 128-byte line (K steps s, s + 1).  Step s's operand needs row c,
-// bytes 16 * g in lane (g, c); step s + 1's row c, bytes 64 + 16 * g.  So
-// step s is x0's lanes 0-7 of each 16-lane row with x1's lanes 0-7 moved up
-// by 8, and step s + 1 is x1's lanes 8-15 with x0's lanes 8-15 moved down by
-// 8: one DPP row shift per dword, the bank mask picking the moved half.
-constexpr int kDppRowShr8 = 0x118, kDppRowShl8 = 0x108;
-__device__ __forceinline__ void line_pair_to_steps(uint4& x0, uint4& x1) {
-  auto lo = [](uint32_t keep, uint32_t from) {  // lanes 8-15 <- from's lanes 0-7
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShr8, 0xF, 0xC, false);
-  };
-  auto hi = [](uint32_t keep, uint32_t from) {  // lanes 0-7 <- from's lanes 8-15
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShl8, 0xF, 0x3, false);
-  };
-  const uint4 s0 = make_uint4(lo(x0.x, x1.x), lo(x0.y, x1.y), lo(x0.z, x1.z), lo(x0.w, x1.w));
-  const uint4 s1 = make_uint4(hi(x1.x, x0.x), hi(x1.y, x0.y), hi(x1.z, x0.z), hi(x1.w, x0.w));
-  x0 = s0;
-  x1 = s1;
-}
-
 template <int MODE, int S>
 __global__ __launch_bounds__(kGemmThreads) void expert_gemm_stream(ExpertGemmArgs p, int mt_max,
                                                                     int n_tiles) {

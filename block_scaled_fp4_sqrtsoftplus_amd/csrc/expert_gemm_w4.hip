@@ -125,14 +125,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
   if (!map_expert_tile(p, mt_max, n_tiles, 16, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int K = p.K, N = p.N;
   const int S = K / 128;                    // a multiple of 4
   const size_t wrow_bytes = (size_t)K / 2;
 
-  const uint8_t* wptr[4];
+  // weight tile t: 16 rows from a wave-uniform base; two K steps of its
+  // rows go out as two whole-line loads (lane (grp, col): row col % 8, then
+  // row 8 + col % 8, bytes 64 * (col / 8) + 16 * grp of the line), turned
+  // into the steps' operands by line_pair_to_steps
+  const uint8_t* wtile[4];
+  const uint32_t loff = (uint32_t)((col & 7) * wrow_bytes + 64 * (col >> 3) + 16 * grp);
   const float* sptr[4];
   int n0;
   bool wave_live = true;
@@ -140,10 +145,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     n0 = n_tile * kG1Cols;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = n0 + 32 * wv + 16 * (t & 1) + col;
+      const int row0 = n0 + 32 * wv + 16 * (t & 1);
+      const int row = row0 + col;
       const uint8_t* base = (t < 2) ? p.w : p.w3;
       const float* sbase = reinterpret_cast<const float*>((t < 2) ? p.w_scale : p.w3_scale);
-      wptr[t] = base + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      wtile[t] = base + ((size_t)e * N + row0) * wrow_bytes;
       sptr[t] = sbase + ((size_t)e * N + row) * S;
     }
   } else {
@@ -151,8 +157,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     wave_live = (n0 + 64 * wv) < N;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = wave_live ? (n0 + 64 * wv + 16 * t + col) : 0;
-      wptr[t] = p.w + ((size_t)e * N + row) * wrow_bytes + grp * 16;
+      const int row0 = wave_live ? (n0 + 64 * wv + 16 * t) : 0;
+      const int row = row0 + col;
+      wtile[t] = p.w + ((size_t)e * N + row0) * wrow_bytes;
       sptr[t] = reinterpret_cast<const float*>(p.w_scale) + ((size_t)e * N + row) * S;
     }
   }
@@ -175,11 +182,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     uint32_t BSW;              // activation scale bytes of steps s0..s0+3
     const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
                         0x08080808, 0x08080808, 0x08080808, 0x08080808};
-    auto load_step = [&](int s, v4u (&a)[4], v4u (&b)[2]) {
+    // steps s, s + 1 (s even): the weight lines of the two steps (rows 0-7 of
+    // each tile into a0, rows 8-15 into a1, non-temporal), and each step's
+    // activation bytes
+    const size_t w8 = 8 * wrow_bytes;
+    auto load_pair = [&](int s, v4u (&a0)[4], v4u (&b0)[2], v4u (&a1)[4], v4u (&b1)[2]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
-      b[0] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128);
-      b[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = wload<v4u>(wtile[t] + loff + (size_t)s * 64);
+        a1[t] = wload<v4u>(wtile[t] + w8 + loff + (size_t)s * 64);
+      }
+      b0[0] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128);
+      b0[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 16);
+      b1[0] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 128);
+      b1[1] = *reinterpret_cast<const v4u*>(bptr + (size_t)s * 128 + 144);
     };
     auto load_scales = [&](int s0) {
       if constexpr (!LINE) {
@@ -220,16 +236,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
       if constexpr (decltype(load)::value) load_scales(s0 + 4);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        if ((d & 1) == 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) line_pair_to_steps(A[d][t], A[d + 1][t]);
+        }
         compute(A[d], sw, d, B[d], bsw);
-        // refill two steps at a time, back to back: the two 64-byte halves
-        // of a weight row's 128-byte line are then requested together, and
-        // the second one meets the first one's line fill (requested a step
-        // apart, the second half missed again: ~25% more HBM reads)
+        // refill two steps at a time (one weight line pair)
         if constexpr (decltype(load)::value) {
-          if (d & 1) {
-            load_step(s0 + 3 + d, A[d - 1], B[d - 1]);
-            load_step(s0 + 4 + d, A[d], B[d]);
-          }
+          if (d & 1) load_pair(s0 + 3 + d, A[d - 1], B[d - 1], A[d], B[d]);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each refill behind its compute
       }
@@ -243,11 +257,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
       }
     }
     load_scales(0);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      load_step(d, A[d], B[d]);
-      __builtin_amdgcn_sched_barrier(0);     // same issue order as in the loop
-    }
+    load_pair(0, A[0], B[0], A[1], B[1]);
+    __builtin_amdgcn_sched_barrier(0);   // same issue order as in the loop
+    load_pair(2, A[2], B[2], A[3], B[3]);
+    __builtin_amdgcn_sched_barrier(0);
     for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
     group(S - 4, std::false_type{});
   }

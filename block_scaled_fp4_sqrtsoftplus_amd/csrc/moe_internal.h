@@ -95,6 +95,33 @@ __device__ __forceinline__ uint4 wload16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Two line loads of a 16-row weight tile: x0 lane (g, c) holds row c % 8,
+// x1 lane (g, c) row 8 + c % 8, both at bytes 64 * (c / 8) + 16 * g of the
+// rows' 128-byte line (K steps s, s + 1 of a 4-bit operand; bytes 0-63 and
+// 64-127 of one step of an 8-bit one).  The MFMA operand of step s needs row
+// c, bytes 16 * g in lane (g, c); that of step s + 1 row c, bytes 64 + 16 * g.
+// So step s is x0's lanes 0-7 of each 16-lane row with x1's lanes 0-7 moved
+// up by 8, and step s + 1 is x1's lanes 8-15 with x0's lanes 8-15 moved down
+// by 8: one DPP row shift per dword, the bank mask picking the moved half.
+// V: any 4 x 32-bit vector with .x .y .z .w.
+constexpr int kDppRowShr8 = 0x118, kDppRowShl8 = 0x108;
+__device__ __forceinline__ uint32_t dpp_up8(uint32_t keep, uint32_t from) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShr8, 0xF, 0xC, false);
+}
+__device__ __forceinline__ uint32_t dpp_down8(uint32_t keep, uint32_t from) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)from, kDppRowShl8, 0xF, 0x3, false);
+}
+template <class V>
+__device__ __forceinline__ void line_pair_to_steps(V& x0, V& x1) {
+  V s0 = x0, s1 = x1;
+  s0.x = dpp_up8(x0.x, x1.x); s0.y = dpp_up8(x0.y, x1.y);
+  s0.z = dpp_up8(x0.z, x1.z); s0.w = dpp_up8(x0.w, x1.w);
+  s1.x = dpp_down8(x1.x, x0.x); s1.y = dpp_down8(x1.y, x0.y);
+  s1.z = dpp_down8(x1.z, x0.z); s1.w = dpp_down8(x1.w, x0.w);
+  x0 = s0;
+  x1 = s1;
+}
+
 // FP8 E4M3 quantization of the 128-element block blk of a bf16 array (one
 // power-of-two scale per block, smallest with amax <= 448 * 2^e): 16 lanes
 // (sub = 0..15, consecutive lanes of one wave) take 8 elements each.  Blocks
