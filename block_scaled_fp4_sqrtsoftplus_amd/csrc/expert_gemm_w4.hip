@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
   __shared__ __attribute__((aligned(16))) uint8_t bsl[kW4M][32];
   __shared__ float red[8][kW4M];
   int n_tile, e, m0, off_e, n_e;
-  if (!map_expert_tile(p, mt_max, n_tiles, kW4M, n_tile, e, m0, off_e, n_e)) return;
+  if (!map_expert_tile_em(p, n_tiles, kW4M, n_tile, e, m0, off_e, n_e)) return;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;

@@ -295,6 +295,43 @@ __device__ __forceinline__ bool map_expert_tile(const ExpertGemmArgs& p, int mt_
   return true;
 }
 
+// Expert-major variant (the 64-pair kernels of the NVFP4 and W4AFP8 formats):
+// the tile list runs over (expert, n-tile, m-tile of the expert) in that
+// order and is dealt to the 8 XCDs in contiguous eighths (workgroup ids go
+// round-robin over the XCDs), so the workgroups an XCD runs at one time
+// cover a few experts: an expert's m-tiles of one n-tile run together (its
+// weights come into that XCD's L2 once) and its n-tiles follow one another
+// (its activation rows stay there).  Workgroups past the list (the grid is
+// sized for the host's upper bound of m-tiles) return false.
+__device__ __forceinline__ bool map_expert_tile_em(const ExpertGemmArgs& p, int n_tiles, int bm,
+                                                   int& n_tile, int& e, int& m0, int& off_e,
+                                                   int& n_e) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  int v[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) v[j] = p.mtile_off[min(lane + 64 * j, p.E)];
+  const int total = __builtin_amdgcn_readfirstlane(p.mtile_off[p.E]) * n_tiles;
+  const int share = (total + 7) >> 3;   // <= gridDim.x / 8: the grid covers the bound
+  const int r = b >> 3;
+  const int u = (b & 7) * share + r;
+  if (r >= share || u >= total) return false;
+  // the expert: the last entry e with mtile_off[e] * n_tiles <= u (empty
+  // experts share their offset with the next one and are passed over)
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) cnt += __popcll(__ballot(lane + 64 * j <= p.E && v[j] * n_tiles <= u));
+  e = cnt - 1;
+  const int mt0 = __builtin_amdgcn_readfirstlane(p.mtile_off[e]);
+  const int m_e = __builtin_amdgcn_readfirstlane(p.mtile_off[e + 1]) - mt0;
+  const int local = u - mt0 * n_tiles;
+  n_tile = local / m_e;
+  m0 = (local - n_tile * m_e) * bm;
+  off_e = p.expert_offsets[e];
+  n_e = p.expert_offsets[e + 1] - off_e;
+  return true;
+}
+
 // bm = tokens per workgroup tile (16 or 64); mt_max = upper bound of m-tiles.
 hipError_t launch_expert_gemm1(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
 hipError_t launch_expert_gemm2(const ExpertGemmArgs& a, int bm, int mt_max, hipStream_t st);
