@@ -62,7 +62,7 @@ def check_routing_valid(r, T, k, E):
     ("decode", 5, dict(n_experts=12)),
     ("decode", 300, dict(hidden=1024, inter=1024, n_experts=4, top_k=2, shared=True)),
     # a larger shared expert through the 128 x 128 bf16 tiles: ragged T (1100 =
-    # 8 x 128 + 76), one up and eight down workgroup columns
+    # 8 x 128 + 76), four up and eight down workgroup columns
     ("decode", 1100, dict(hidden=1024, inter=256, n_experts=4, top_k=2, shared=True)),
     # decode-sized shared expert through the split-K kernels (T <= 64, H and I
     # multiples of 512) on the side stream: ragged T, a full 64-token batch,
