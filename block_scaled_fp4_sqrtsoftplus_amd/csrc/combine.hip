@@ -31,16 +31,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     pp[j] = pair_pos[t * K + j];
     wj[j] = w[t * K + j];
   }
-  float4 v[K];
+  // the rows of o are read once, a wave taking 1 KB of one row: whole-line
+  // non-temporal loads (wload)
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  f4v v[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const float4*>(o + (size_t)pp[j] * H + c);
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (ysh) {
+  for (int j = 0; j < K; ++j) v[j] = wload<f4v>(o + (size_t)pp[j] * H + c);
+  f4v s = {0.f, 0.f, 0.f, 0.f};
+  if (ysh) {   // read once too
     const float* p = ysh + (size_t)t * H + c;
     const size_t stride = (size_t)T * H;
-    s = *reinterpret_cast<const float4*>(p);
+    s = wload<f4v>(p);
     for (int i = 1; i < parts; ++i) {
-      const float4 b = *reinterpret_cast<const float4*>(p + i * stride);
+      const f4v b = wload<f4v>(p + i * stride);
       s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
     }
   }
