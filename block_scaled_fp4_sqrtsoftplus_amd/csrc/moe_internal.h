@@ -79,7 +79,8 @@ __device__ __forceinline__ float clamp_sym(float x, float lim) {
   return __builtin_amdgcn_fmed3f(x, -lim, lim);
 }
 
-// Load of streamed weight bytes: a non-temporal global load (the nt bit).
+// Load of bytes that are read exactly once per call (streamed weights, the
+// combine's expert rows): a non-temporal global load (the nt bit).
 // Measured on MI355X: a 2 GiB read in 1 KB-contiguous wave loads streams at
 // 6.2-6.3 TB/s with ordinary loads and 7.0-7.1 TB/s with nt; loads of 8 rows
 // x 128 bytes (whole lines) 5.7 -> 6.5 TB/s; but loads that take half of
