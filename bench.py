@@ -27,6 +27,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # dense FP8 (an FP4 x FP8 scaled MFMA issues at most at this rate)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 EXPERT_BYTES = None              # set from the workload
+WEIGHT_COPIES = 2                # weight sets the timed calls rotate through
 
 
 def parse():
@@ -176,7 +177,17 @@ def measure(args, wl, steps, with_graph=True, with_cpu=False):
         for n in ("w1_scale", "w3_scale", "w2_scale"):
             w[n] = d(inp[n])
         cfg.expert_format = moe.EXPERTS_W4AFP8
-    L = moe.Layer(cfg, w, w_gate=wg, bias=bias, shared=shared)
+    # Two copies of every weight (experts, gate, shared expert), used in
+    # turn: no weight byte one timed call reads is still in the caches for the
+    # next, as in a model whose consecutive layers have different weights
+    # (with one copy, back-to-back calls read ~3% of the decode weights from
+    # the last-level cache of the call before).
+    clone = lambda t: None if t is None else t.clone()
+    ws_copies = [w, {n: t.clone() for n, t in w.items()}]
+    wg_copies = [wg, clone(wg)]
+    sh_copies = [shared, None if shared is None else {n: t.clone() for n, t in shared.items()}]
+    layers = [moe.Layer(cfg, ws_copies[i], w_gate=wg_copies[i], bias=bias, shared=sh_copies[i])
+              for i in range(WEIGHT_COPIES)]
     y = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device=dev)
     routing = moe._routing_tensors(wl.tokens, wl.top_k, wl.n_experts, dev)
     print(f"[bench] {wl.name}: inputs ready in {time.time() - t0:.1f}s: {wl}", file=sys.stderr,
@@ -195,14 +206,24 @@ def measure(args, wl, steps, with_graph=True, with_cpu=False):
         torch.cuda.synchronize()
         return (time.perf_counter() - t_start) * 1e3 / n, ev0.elapsed_time(ev1) / n
 
+    def rotating(fns):
+        state = {"i": 0}
+
+        def call():
+            fns[state["i"] % len(fns)]()
+            state["i"] += 1
+        return call
+
     # whole layer: eager calls (the step), then replays of the same call
-    # captured into a HIP graph
-    eager_ms, eager_gpu_ms = timed(lambda: L(x, ids, y=y, routing=routing), steps)
+    # captured into a HIP graph (one graph per weight copy)
+    eager_ms, eager_gpu_ms = timed(
+        rotating([lambda L=L: L(x, ids, y=y, routing=routing) for L in layers]), steps)
     graph_ms = graph_gpu_ms = None
     if with_graph:
-        graph = moe.LayerGraph(L, x, token_ids=ids, y=y, routing=routing)
-        graph_ms, graph_gpu_ms = timed(graph.launch, steps)
-        graph.close()
+        graphs = [moe.LayerGraph(L, x, token_ids=ids, y=y, routing=routing) for L in layers]
+        graph_ms, graph_gpu_ms = timed(rotating([g.launch for g in graphs]), steps)
+        for g in graphs:
+            g.close()
     load = np.diff(routing["expert_offsets"].cpu().numpy())
     n_touched = int(np.sum(load > 0))
 
@@ -213,16 +234,17 @@ def measure(args, wl, steps, with_graph=True, with_cpu=False):
     ffn_out = torch.empty((wl.tokens * wl.top_k, wl.hidden), dtype=torch.float32, device=dev)
     ws_n = moe.workspace_size(cfg, moe.OP_EXPERT_FFN)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-    cc, rc, wc = cfg.c(), moe._routing_c(routing), moe._weights_c(w)
+    cc, rc = cfg.c(), moe._routing_c(routing)
+    wcs = [moe._weights_c(wi) for wi in ws_copies]
 
-    def ffn_call():
+    def ffn_call(wc):
         st = moe.lib.moe_expert_ffn(ctypes.byref(cc), moe._ptr(xq), moe._ptr(xs), ctypes.byref(rc),
                                     ctypes.byref(wc), moe._ptr(ffn_out), None, None,
                                     moe._ptr(ws), ws_n, moe._stream())
         if st != 0:
             raise moe.MoeError(st)
 
-    _, ffn_ms = timed(ffn_call, steps)
+    _, ffn_ms = timed(rotating([lambda wc=wc: ffn_call(wc) for wc in wcs]), steps)
 
     alg = algorithmic(wl, n_touched, args.experts)
     # the NVFP4 path dequantizes to fp16 and runs on the fp16 MFMA (the bf16 / fp16 peak)
