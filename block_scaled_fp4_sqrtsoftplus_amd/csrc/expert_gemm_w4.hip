@@ -8,8 +8,10 @@
 // exactly u * 2^-9 (subnormals below 8, exponent field 1 from 8 up), so with
 // a block scale of 2^9 on that operand the step's MFMA gives
 // sum_k (q_k + 8) x_k.  One more MFMA per step, against a constant operand of
-// code 8, gives 8 sum_k x_k per token; it is subtracted before the row's
-// float32 group scale multiplies the step's result into the accumulator.
+// code 0x88 (-8 * 2^-9), gives -8 sum_k x_k per token, which enters the
+// step's weight MFMAs as their accumulator input, so that they return
+// sum_k q_k x_k; the row's float32 group scale then multiplies that into the
+// accumulator.
 // The products u * x are exact (4 x 4 significant bits) and the per-step
 // sums are fp32, as in the other expert GEMMs.
 //
@@ -40,36 +42,56 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// D = A . B with E8M0 block scales sa (A) and sb (B), from zero.  The asm
-// leaves 2 wait states between the VALU instructions that build the
-// operands and the MFMA (the compiler cannot insert them in front of an asm;
-// without them the MFMA read a stale B register), and the scale registers
-// and the result untouched for 32 wait states after it, as in the FP4
+// The MFMA groups below (E8M0 block scales sa on A, sb on B) leave 2 wait
+// states between the VALU instructions that build the operands and the
+// first MFMA (the compiler cannot insert them in front of an asm; without
+// them the MFMA read a stale B register), and the scale registers and the
+// results untouched for 32 wait states after the last, as in the FP4
 // kernels.
-__device__ __forceinline__ v4f mfma_w4(const v8i& a, const v8i& b, int sa, int sb) {
-  v4f d;
+
+// Five MFMAs for one 16-pair step: c = a . neg8 from zero (neg8: E4M3 code
+// 0x88 = -8 * 2^-9, so with the 2^9 block scale c = -8 sum x per token), then
+// d[t] = a . b[t] + c for the four weight tiles; the corrected sums come out
+// of the matrix pipe (as in mfma_w4x12 below).
+__device__ __forceinline__ void mfma_w4x5(const v8i& a, const v8i& neg8, const v8i (&b)[4], int sa,
+                                          int sb, v4f& c, v4f (&d)[4]) {
+#define W4X5_ROW(T)                                                                        \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[d" #T "], %[a], %[b" #T "], %[c], %[s], %[t] op_sel_hi:[0,0,0]\n\t"
   asm volatile(
       "s_nop 1\n\t"
-      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %[c], %[a], %[e], 0, %[s], %[t] op_sel_hi:[0,0,0]\n\t"
+      "s_nop 1\n\t"
+      W4X5_ROW(0) W4X5_ROW(1) W4X5_ROW(2) W4X5_ROW(3)
       "s_nop 15\n\t"
       "s_nop 15"
-      : "=&v"(d)
-      : "v"(a), "v"(b), "v"(sa), "v"(sb));
-  return d;
+      : [c] "=&v"(c), [d0] "=&v"(d[0]), [d1] "=&v"(d[1]), [d2] "=&v"(d[2]), [d3] "=&v"(d[3])
+      : [a] "v"(a), [e] "v"(neg8), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
+        [b3] "v"(b[3]), [s] "v"(sa), [t] "v"(sb));
+#undef W4X5_ROW
 }
 
-// Twelve MFMAs from zero: for the four activation operands a[m] (block
-// scales sa[m]), c[m] = a[m] . eights, d0[m] = a[m] . b0, d1[m] = a[m] . b1;
-// one 2-wait-state lead and one 32-wait-state guard for the group, so the
-// matrix pipe gets all twelve back to back.
-__device__ __forceinline__ void mfma_w4x12(const v8i (&a)[4], const v8i& eights, const v8i& b0,
+// Twelve MFMAs: for the four activation operands a[m] (block scales sa[m]),
+// c[m] = a[m] . neg8 from zero (neg8: E4M3 code 0x88 = -8 * 2^-9, so with
+// the 2^9 block scale c[m] = -8 sum x per token), then d0[m] = a[m] . b0 +
+// c[m] and d1[m] = a[m] . b1 + c[m]: the step's sums with the correction
+// already applied, taken as the MFMAs' accumulator input (exactly the
+// registers the correction MFMA wrote, which the matrix pipe interlocks like
+// an accumulation chain; a 32-wait-state gap there measured slower and gave
+// the same bits).  One 2-wait-state lead, one 32-wait-state guard for the
+// group.  Result: the same bits as subtracting c[m] from the two sums
+// afterwards, one VALU op less per result and step, and GEMM2's kernel
+// (which spilled with the subtraction) within its registers.
+__device__ __forceinline__ void mfma_w4x12(const v8i (&a)[4], const v8i& neg8, const v8i& b0,
                                            const v8i& b1, const int (&sa)[4], int sb,
                                            v4f (&c)[4], v4f (&d0)[4], v4f (&d1)[4]) {
+#define W4X12_CORR(M)                                                                      \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[c" #M "], %[a" #M "], %[e], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t"
 #define W4X12_ROW(M)                                                                      \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[c" #M "], %[a" #M "], %[e], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[x" #M "], %[a" #M "], %[b0], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t" \
-  "v_mfma_scale_f32_16x16x128_f8f6f4 %[y" #M "], %[a" #M "], %[b1], 0, %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t"
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[x" #M "], %[a" #M "], %[b0], %[c" #M "], %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t" \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %[y" #M "], %[a" #M "], %[b1], %[c" #M "], %[s" #M "], %[t] op_sel_hi:[0,0,0]\n\t"
   asm volatile(
+      "s_nop 1\n\t"
+      W4X12_CORR(0) W4X12_CORR(1) W4X12_CORR(2) W4X12_CORR(3)
       "s_nop 1\n\t"
       W4X12_ROW(0) W4X12_ROW(1) W4X12_ROW(2) W4X12_ROW(3)
       "s_nop 15\n\t"
@@ -77,9 +99,10 @@ __device__ __forceinline__ void mfma_w4x12(const v8i (&a)[4], const v8i& eights,
       : [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]),
         [x0] "=&v"(d0[0]), [x1] "=&v"(d0[1]), [x2] "=&v"(d0[2]), [x3] "=&v"(d0[3]),
         [y0] "=&v"(d1[0]), [y1] "=&v"(d1[1]), [y2] "=&v"(d1[2]), [y3] "=&v"(d1[3])
-      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [e] "v"(eights),
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [e] "v"(neg8),
         [b0] "v"(b0), [b1] "v"(b1), [s0] "v"(sa[0]), [s1] "v"(sa[1]), [s2] "v"(sa[2]),
         [s3] "v"(sa[3]), [t] "v"(sb));
+#undef W4X12_CORR
 #undef W4X12_ROW
 }
 
@@ -93,6 +116,13 @@ __device__ __forceinline__ v8i int4_operand(const v4u& w) {
              (int)(y1 & 0x0F0F0F0Fu), (int)((y1 >> 4) & 0x0F0F0F0Fu),
              (int)(y2 & 0x0F0F0F0Fu), (int)((y2 >> 4) & 0x0F0F0F0Fu),
              (int)(y3 & 0x0F0F0F0Fu), (int)((y3 >> 4) & 0x0F0F0F0Fu)};
+}
+
+// 16 activation bytes (elements 0..15 in order) -> the same slot order:
+// dword 2i the even elements 8i, 8i+2, 8i+4, 8i+6, dword 2i+1 the odd ones
+__device__ __forceinline__ v4u act_slots16(const v4u& b) {
+  return v4u{__builtin_amdgcn_perm(b.y, b.x, 0x06040200u), __builtin_amdgcn_perm(b.y, b.x, 0x07050301u),
+             __builtin_amdgcn_perm(b.w, b.z, 0x06040200u), __builtin_amdgcn_perm(b.w, b.z, 0x07050301u)};
 }
 
 // 32 activation bytes (elements 0..31 in order) -> the same slot order
@@ -180,8 +210,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
     v4u SW[4];                 // !LINE: float32 scales of steps s0..s0+3, per tile
     v4u SL[4][2];              // LINE: scales of steps 8 grp .. 8 grp + 7, per tile
     uint32_t BSW;              // activation scale bytes of steps s0..s0+3
-    const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
-                        0x08080808, 0x08080808, 0x08080808, 0x08080808};
+    const v8i neg8 = {(int)0x88888888u, (int)0x88888888u, (int)0x88888888u, (int)0x88888888u,
+                      (int)0x88888888u, (int)0x88888888u, (int)0x88888888u, (int)0x88888888u};
     // steps s, s + 1 (s even): the weight lines of the two steps (rows 0-7 of
     // each tile into a0, rows 8-15 into a1, non-temporal), and each step's
     // activation bytes
@@ -208,13 +238,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
                        uint32_t bsw) {
       const int sa = (int)((bsw >> (8 * d)) & 0xFFu);
       const v8i xa = act_operand(b[0], b[1]);
-      const v4f corr = mfma_w4(xa, eights, sa, kW4ScaleB);
+      v8i wb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wb[t] = int4_operand(a[t]);
+      v4f c, part[4];
+      mfma_w4x5(xa, neg8, wb, sa, kW4ScaleB, c, part);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const v4f part = mfma_w4(xa, int4_operand(a[t]), sa, kW4ScaleB);
         const float s = __uint_as_float(sw[t][d]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(part[v] - corr[v], s, acc[t][v]);
+        for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(part[t][v], s, acc[t][v]);
       }
     };
     // one group of four steps; LOAD: refill the ring with the next group
@@ -326,9 +359,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_w4(ExpertGemmArgs
 // ---------------------------------------------------------------------------
 // Eight waves of 32 weight rows (GEMM1: 16 h columns, their w1 and w3 rows;
 // GEMM2: 32 output columns), the register ring of weight steps as above.
-// The m-tile's 64 activation rows of a K step are staged once in LDS (double
-// buffer; 16-byte chunks xor-swizzled by row, so that the 16 rows a wave
-// reads at one offset hit distinct banks) and every wave takes four 16-pair
+// The m-tile's 64 activation rows of a K step are staged once in LDS, already
+// in the MFMA's slot order (double buffer; 16-byte chunks xor-swizzled by
+// row, so that the 16 rows a wave reads at one offset hit distinct banks;
+// permuting once while staging instead of in every wave's operand reads:
+// -5% time) and every wave takes four 16-pair
 // sub-tiles from there: each unpacked weight operand feeds four MFMAs.  The
 // waves' float32 scale lines (rows padded to 33) and the 64 tokens'
 // activation scales stay in LDS for the whole tile; one barrier per K step.
@@ -408,8 +443,8 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[t][m] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const v8i eights = {0x08080808, 0x08080808, 0x08080808, 0x08080808,
-                      0x08080808, 0x08080808, 0x08080808, 0x08080808};
+  const v8i neg8 = {(int)0x88888888u, (int)0x88888888u, (int)0x88888888u, (int)0x88888888u,
+                    (int)0x88888888u, (int)0x88888888u, (int)0x88888888u, (int)0x88888888u};
   v4u A[4][2];     // weight ring: [step][tile]
   v4u R;           // the chunk of the next step to stage
   auto load_w = [&](int s, v4u (&a)[2]) {
@@ -417,7 +452,7 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
     for (int t = 0; t < 2; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
   };
   auto load_x = [&](int s) { R = *reinterpret_cast<const v4u*>(xsrc + (size_t)s * 128); };
-  auto store_x = [&](int buf) { *reinterpret_cast<v4u*>(&xl[buf][xc]) = R; };
+  auto store_x = [&](int buf) { *reinterpret_cast<v4u*>(&xl[buf][xc]) = act_slots16(R); };
 
   // one K step from the weight ring slot a and LDS buffer buf
   auto compute = [&](int s, const v4u (&a)[2], int buf) {
@@ -430,17 +465,18 @@ __global__ __launch_bounds__(kW4MThreads, 2) void expert_gemm_w4_m64(ExpertGemmA
       const uint8_t* xr = &xl[buf][(16 * m + col) * 128];
       const v4u lo = *reinterpret_cast<const v4u*>(xr + ((2 * grp) ^ (col & 7)) * 16);
       const v4u hi = *reinterpret_cast<const v4u*>(xr + ((2 * grp + 1) ^ (col & 7)) * 16);
-      xa[m] = act_operand(lo, hi);
+      xa[m] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sa[m] = bsl[16 * m + col][s];
     }
     v4f c[4], d0[4], d1[4];
-    mfma_w4x12(xa, eights, b0, b1, sa, kW4ScaleB, c, d0, d1);
+    mfma_w4x12(xa, neg8, b0, b1, sa, kW4ScaleB, c, d0, d1);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        acc[0][m][v] = __builtin_fmaf(d0[m][v] - c[m][v], sw0, acc[0][m][v]);
-        acc[1][m][v] = __builtin_fmaf(d1[m][v] - c[m][v], sw1, acc[1][m][v]);
+        acc[0][m][v] = __builtin_fmaf(d0[m][v], sw0, acc[0][m][v]);
+        acc[1][m][v] = __builtin_fmaf(d1[m][v], sw1, acc[1][m][v]);
       }
   };
   // one group of four steps; LOAD: refill the weight ring with the next group
