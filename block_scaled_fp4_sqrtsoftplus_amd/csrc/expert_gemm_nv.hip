@@ -319,7 +319,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void expert_gemm_nv(ExpertGemmArgs
 // distinct banks), and every wave takes four 16-pair sub-tiles from there:
 // each dequantized weight operand feeds four MFMAs.  The waves' scale lines
 // (staged as in the LINE streaming kernel) and the 64 tokens' activation
-// scales stay in LDS for the tile; one barrier per K step.
+// scales stay in LDS for the tile; one barrier per K step.  Tiles whose
+// activation scales all lie in the range fp16 can carry exactly are staged
+// with the scales applied and accumulate in the MFMAs; the others stage the
+// unscaled codes and scale each step's sums on the VALU (see the kernel).
 constexpr int kNvM = 64;
 constexpr int kNvMThreads = 512;
 
@@ -390,6 +393,23 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
       }
   }
 
+  // Scaled staging: when every activation scale of the tile is 2^e with
+  // -15 <= e <= 7, the staged fp16 values can carry their scale exactly
+  // (448 * 2^7 < 65504, and the E4M3 grid step 2^-9 times 2^-15 is still
+  // an fp16 subnormal step), so the MFMAs accumulate straight into acc; else
+  // the unscaled codes, each step's sums then scaled into acc (exact powers
+  // of two) by the VALU.
+  bool scaled_ok = true;
+  {
+    const int b0 = min(4 * sq, S - 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = p.a_scale[stok * S + b0 + j];
+      scaled_ok = scaled_ok && c >= 127 - 15 && c <= 127 + 7;
+    }
+  }
+  const bool scaled = __syncthreads_and(scaled_ok);
+
   v4f acc[2][4];   // [weight tile][16-pair sub-tile]
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -403,13 +423,21 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
     for (int t = 0; t < 2; ++t) a[t] = *reinterpret_cast<const v4u*>(wptr[t] + (size_t)s * 64);
   };
   auto load_x = [&](int s) { R = *reinterpret_cast<const v4u*>(xsrc + (size_t)s * 128); };
-  auto store_x = [&](int buf) {
-    *reinterpret_cast<h8*>(&xl[buf][xc0]) = fp8x8_to_f16(R.x, R.y);
-    *reinterpret_cast<h8*>(&xl[buf][xc1]) = fp8x8_to_f16(R.z, R.w);
+  // the rows of step s (in R) into LDS buffer buf; SC: times 2^(e_s - 127)
+  auto store_x = [&](int buf, int s, auto sc) {
+    h8 lo = fp8x8_to_f16(R.x, R.y), hi = fp8x8_to_f16(R.z, R.w);
+    if constexpr (decltype(sc)::value) {
+      const _Float16 f = (_Float16)__uint_as_float((uint32_t)bsl[sr][s] << 23);
+      const h8 fv = {f, f, f, f, f, f, f, f};
+      lo = lo * fv;
+      hi = hi * fv;
+    }
+    *reinterpret_cast<h8*>(&xl[buf][xc0]) = lo;
+    *reinterpret_cast<h8*>(&xl[buf][xc1]) = hi;
   };
   // one K step from the weight ring slot a and LDS buffer buf: MFMA j of a
   // 16 x 16 tile takes elements 32 grp + 8 j .. +7 of the step
-  auto compute = [&](int s, const v4u (&a)[2], int buf) {
+  auto compute = [&](int s, const v4u (&a)[2], int buf, auto sc) {
     h8 wb[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -429,26 +457,34 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         bo[j] = *reinterpret_cast<const h8*>(xr + ((4 * grp + j) ^ (r & 15)) * 16);
-      const float sx = __uint_as_float((uint32_t)bsl[r][s] << 23);   // 2^(code - 127)
+      if constexpr (decltype(sc)::value) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v4f part = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb[t][j], bo[j], part, 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb[t][j], bo[j], acc[t][m], 0, 0, 0);
+      } else {
+        const float sx = __uint_as_float((uint32_t)bsl[r][s] << 23);   // 2^(code - 127)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][m][v] = __builtin_fmaf(part[v], sx, acc[t][m][v]);
+        for (int t = 0; t < 2; ++t) {
+          v4f part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb[t][j], bo[j], part, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][m][v] = __builtin_fmaf(part[v], sx, acc[t][m][v]);
+        }
       }
     }
   };
   // one group of four steps; LOAD: refill the weight ring with the next group
   // (two steps at a time: both halves of each 128-byte line back to back)
-  auto group = [&](int s0, auto load) {
+  auto group = [&](int s0, auto load, auto sc) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int s = s0 + d;
-      compute(s, A[d], s & 1);
-      store_x((s + 1) & 1);                 // step s + 1 (the last step's copy is unused)
+      compute(s, A[d], s & 1, sc);
+      store_x((s + 1) & 1, min(s + 1, S - 1), sc);   // step s + 1 (the last step's copy is unused)
       load_x(min(s + 2, S - 1));
       if constexpr (decltype(load)::value) {
         if (d & 1) {
@@ -461,14 +497,20 @@ __global__ __launch_bounds__(kNvMThreads, 1) void expert_gemm_nv_m64(ExpertGemmA
     }
   };
 
-  load_x(0);
-  store_x(0);
-  load_x(min(1, S - 1));
+  auto k_loop = [&](auto sc) {
+    load_x(0);
+    store_x(0, 0, sc);
+    load_x(min(1, S - 1));
 #pragma unroll
-  for (int d = 0; d < 4; ++d) load_w(d, A[d]);
-  __syncthreads();
-  for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{});
-  group(S - 4, std::false_type{});
+    for (int d = 0; d < 4; ++d) load_w(d, A[d]);
+    __syncthreads();
+    for (int s0 = 0; s0 < S - 4; s0 += 4) group(s0, std::true_type{}, sc);
+    group(S - 4, std::false_type{}, sc);
+  };
+  if (scaled)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
 
   // lane holds acc[t][m][v] = output (weight row 4 grp + v of tile t, token
   // 16 m + col)

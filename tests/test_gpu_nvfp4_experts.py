@@ -50,6 +50,40 @@ def test_nvfp4_expert_ffn_parity(shape):
     _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
 
 
+def _scale_bf16(x16, k):
+    """bf16 bits times 2^k (exact: only the exponent field moves)."""
+    x32 = (x16.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+    out = (x32.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((out.astype(np.uint32) << 16).view(np.float32), x32)
+    return out
+
+
+@pytest.mark.parametrize("k", [-24, 16])
+def test_nvfp4_expert_ffn_activation_scale_range(k):
+    """The 64-pair kernel stages activations with their power-of-two scale
+    applied in fp16 only while every scale of the tile is 2^e, -15 <= e <= 7;
+    activations far outside (here x times 2^-24: GEMM1 and, through the tiny
+    h, GEMM2; x times 2^16: GEMM1) take the unscaled staging instead."""
+    wl = synth.WORKLOADS["tiny"].replace(hidden=512, inter=1024, n_experts=6, top_k=2)
+    inp = _nv_inputs(wl, 200)
+    inp["x"] = _scale_bf16(inp["x"], k)
+    xq, xs = quant.act_quant(formats.bf16_decode(inp["x"]))
+    e = xs.astype(np.int64) - 127
+    assert (e < -15).any() if k < 0 else (e > 7).any()
+    r = oroute.route(inp["x"], inp["w_gate"], k=wl.top_k, route_scale=wl.route_scale)
+    ref = ffn.expert_ffn(xq, xs, r, inp, wl.top_k, wl.swiglu_limit, weight_format="nvfp4")
+    T = inp["x"].shape[0]
+    cfg = config(moe, wl, tokens=T, expert_format=moe.EXPERTS_NVFP4)
+    routing = {n: dev(r[n]) for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_pos")}
+    w = {n: dev(inp[n]) for n in ("w1", "w1_scale", "w3", "w3_scale", "w2", "w2_scale")}
+    g = moe.expert_ffn(cfg, dev(xq), dev(xs), routing, w, want_h=True)
+    torch.cuda.synchronize()
+    dh, absw2 = _bounds(inp, xq, xs, r, ref, wl, deq=quant.nvfp4_dequant)
+    hq, hs = host(g["hq"]), host(g["hs"])
+    _check_hq(hq, hs, ref, dh, max_flip_frac=MAX_FLIP_FRAC)
+    _check_o(host(g["out"]).astype(np.float64), hq, hs, ref, r, absw2)
+
+
 @pytest.mark.parametrize("shape", [
     ("tiny", 45, dict(hidden=512, inter=512, n_experts=12, top_k=3, shared=True)),
     ("decode", 5, dict(n_experts=12)),
